@@ -1,0 +1,414 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix (CPU only).
+
+Each test checks the oracle against something other than itself: closed forms, tabulated values,
+brute force over all subsets on tiny inputs, invariants the pages state, or hand-derived numbers.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from synth import LayerSpec, gen_layer_inputs
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _brute_topk(keys_row, k):
+    """Brute force: the k-subset with the largest key sum; ties to the lexicographically smallest
+    sorted index tuple. Keys here are exact in fp64 (small integers or dyadic)."""
+    best, best_sum = None, -math.inf
+    for sub in itertools.combinations(range(len(keys_row)), k):   # lexicographic order
+        s = sum(keys_row[i] for i in sub)
+        if s > best_sum:
+            best, best_sum = sub, s
+    return best
+
+
+# ------------------------------------------------------------------------------ softmax
+
+
+def test_softmax_rows_sum_to_one():
+    rng = np.random.default_rng(1)
+    L = rng.standard_normal((300, 19)) * 3
+    P = orc.softmax(L)
+    assert np.all(P > 0)
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-12
+
+
+def test_softmax_two_experts_is_logistic():
+    g = _gold("logistic.json")
+    for z, sig in g["values"]:
+        # p_0 of a two-expert row [l0, l1] = sigma(l0 - l1); check at several offsets.
+        for base in (-3.0, 0.0, 7.5):
+            P = orc.softmax(np.array([[base + z, base]]))
+            assert abs(P[0, 0] - sig) <= g["tolerance"]
+            assert abs(P[0, 1] - (1 - sig)) <= g["tolerance"]
+
+
+# ------------------------------------------------------------------------------ token choice
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tc_matches_bruteforce_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    S, E = 8, int(rng.integers(2, 9))
+    L = rng.integers(-2, 3, size=(S, E)).astype(float)    # many exact ties
+    for k in range(1, E + 1):
+        idx = orc.tc_select(L, k)
+        for s in range(S):
+            assert tuple(sorted(idx[s])) == _brute_topk(L[s], k)
+            # slots in key order: keys non-increasing, equal keys by ascending index
+            for a, b in zip(idx[s][:-1], idx[s][1:]):
+                assert L[s, a] > L[s, b] or (L[s, a] == L[s, b] and a < b)
+
+
+def test_tc_k_equals_E_selects_all():
+    rng = np.random.default_rng(3)
+    L = rng.standard_normal((50, 7))
+    idx = orc.tc_select(L, 7)
+    assert np.all(np.sort(idx, axis=1) == np.arange(7))
+
+
+def test_tc_weights_renorm_is_softmax_over_chosen():
+    rng = np.random.default_rng(4)
+    L = rng.standard_normal((40, 8))
+    idx = orc.tc_select(L, 2)
+    w = orc.tc_weights(orc.softmax(L), idx, renorm=True)
+    # Closed form for two chosen logits a >= b: weights sigma(a-b), sigma(b-a).
+    a = np.take_along_axis(L, idx[:, :1], 1)[:, 0]
+    b = np.take_along_axis(L, idx[:, 1:2], 1)[:, 0]
+    sig = 1.0 / (1.0 + np.exp(-(a - b)))
+    assert np.allclose(w[:, 0], sig, rtol=0, atol=1e-14)
+    assert np.allclose(w[:, 1], 1 - sig, rtol=0, atol=1e-14)
+    wr = orc.tc_weights(orc.softmax(L), idx, renorm=False)
+    ex = np.exp(L)
+    assert np.allclose(wr, np.take_along_axis(ex, idx, 1) / ex.sum(1, keepdims=True), atol=1e-15)
+
+
+# ------------------------------------------------------------------------------ expert choice
+
+
+def test_capacity_page_values_and_rounding():
+    for c in _gold("page_values.json")["capacity"]["cases"]:
+        assert orc.ec_capacity(c["S"], c["E"], c["f_c"]) == c["C"]
+    assert orc.ec_capacity(10, 3, 2.0) == 6           # 6.67 rounds down
+    assert orc.ec_capacity(10, 1, 2.0) == 10          # clipped to S
+    assert orc.ec_capacity(7, 4, 0.5) == 0            # rounds to 0 (the library rejects this)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_ec_matches_bruteforce(seed):
+    rng = np.random.default_rng(10 + seed)
+    S, E = 8, 4
+    A = rng.integers(0, 6, size=(S, E)) / 8.0          # dyadic, exact sums, ties
+    C = orc.ec_capacity(S, E, 2.0)
+    tokens, gates = orc.ec_select(A, C)
+    for i in range(E):
+        assert tuple(tokens[i]) == _brute_topk(A[:, i], C)
+        assert np.array_equal(gates[i], A[tokens[i], i])
+
+
+def test_ec_natural_balance_and_variable_experts_per_token():
+    rng = np.random.default_rng(5)
+    S, E = 512, 16
+    A = orc.softmax(rng.standard_normal((S, E)))
+    C = orc.ec_capacity(S, E, 2.0)
+    tokens, _ = orc.ec_select(A, C)
+    counts = np.bincount(tokens.ravel(), minlength=S)
+    assert tokens.shape == (E, C) and C == 64
+    assert all(len(set(t)) == C for t in tokens)       # every expert takes exactly C distinct tokens
+    assert counts.sum() == E * C
+    assert counts.min() >= 0 and counts.max() <= E
+    assert counts.min() != counts.max()                # tokens get a variable number of experts
+    off, lst = orc.ec_token_csr(tokens, S)
+    assert np.array_equal(np.diff(off), counts)
+    for s in range(0, S, 37):
+        rows = lst[off[s]:off[s + 1]]
+        experts = rows // C
+        assert np.all(np.diff(experts) > 0)
+        assert np.all(tokens[experts, rows % C] == s)
+
+
+def _dense_spec(**kw):
+    base = dict(name="t", S=24, d=8, f=12, E_heavy=1, act="gelu", mode="tc", k=1, dtype="f32")
+    base.update(kw)
+    return LayerSpec(**base)
+
+
+def _textbook_ffn(x, w1, w3, w2, act):
+    """Dense FFN written from scratch for the E=1 checks (matrix-vector loops)."""
+    y = np.zeros((x.shape[0], w2.shape[0]))
+    for s in range(x.shape[0]):
+        u = np.array([sum(w1[o, i] * x[s, i] for i in range(x.shape[1])) for o in range(w1.shape[0])])
+        if act == "swiglu":
+            g = np.array([sum(w3[o, i] * x[s, i] for i in range(x.shape[1])) for o in range(w3.shape[0])])
+            h = g / (1 + np.exp(-g)) * u
+        else:
+            h = np.array([v * 0.5 * (1 + math.erf(v / math.sqrt(2))) for v in u])
+        y[s] = [sum(w2[o, i] * h[i] for i in range(h.size)) for o in range(w2.shape[0])]
+    return y
+
+
+@pytest.mark.parametrize("mode,act", [("tc", "gelu"), ("tc", "swiglu"), ("ec", "gelu")])
+def test_single_expert_is_dense_mlp(mode, act):
+    spec = _dense_spec(mode=mode, act=act)
+    W = gen_layer_inputs(spec, seed=2, std=0.3)
+    r = orc.layer_forward(spec, W, W.x)
+    if mode == "ec":
+        assert r["rt"]["C"] == spec.S
+        assert np.all(r["rt"]["gates"] == 1.0)
+    ref = _textbook_ffn(W.x.astype(float), W.w1[0][0].astype(float),
+                        None if W.w3[0] is None else W.w3[0][0].astype(float),
+                        W.w2[0][0].astype(float), act)
+    assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------ DES
+
+
+def _des_bruteforce(P, K, M):
+    """Core set by brute force: per token the K-subset of largest probability sum; total vote of a
+    candidate core = sum over tokens of the probabilities of its members inside that token's
+    filtered set; the best M-subset, ties to the lexicographically smallest tuple."""
+    N, E = P.shape
+    T = [set(_brute_topk(P[n], K)) for n in range(N)]
+    best, best_v = None, -math.inf
+    for core in itertools.combinations(range(E), M):
+        v = sum(P[n, e] for n in range(N) for e in core if e in T[n])
+        if v > best_v:
+            best, best_v = core, v
+    return best
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_des_vote_core_matches_bruteforce(seed):
+    rng = np.random.default_rng(20 + seed)
+    N, E = int(rng.integers(2, 7)), int(rng.integers(4, 11))
+    raw = rng.integers(0, 9, size=(N, E)).astype(float)
+    raw[:, 0] += 1
+    P = raw / 1024.0                                   # dyadic "routing weights" (exact sums)
+    K = int(rng.integers(1, E + 1))
+    M = int(rng.integers(1, E + 1))
+    for vdt in (np.float64, np.float32):
+        votes, core = orc.des_vote(P, P, K, M, vote_dtype=vdt)
+        assert core.size == M and np.all(np.diff(core) > 0)
+        assert tuple(core) == _des_bruteforce(P, K, M)
+
+
+def test_des_core_size_page_values():
+    for c in _gold("page_values.json")["core_size"]["cases"]:
+        assert int(c["beta"] * c["M"]) == c["M_core"]
+        rng = np.random.default_rng(0)
+        L = rng.standard_normal((32, c["M"]))
+        _, core = orc.des_vote(L, orc.softmax(L), 8, c["M_core"])
+        assert core.size == c["M_core"]
+
+
+def test_des_beta_one_and_full_cover_equal_token_choice():
+    rng = np.random.default_rng(7)
+    N, E, k = 32, 64, 8
+    L = rng.standard_normal((N, E))
+    P = orc.softmax(L)
+    idx_tc = orc.tc_select(L, k)
+    w_tc = orc.tc_weights(P, idx_tc, True)
+    # beta = 1: the core is every expert
+    _, core = orc.des_vote(L, P, k, E)
+    idx, w = orc.core_reroute(L, P, core, k, True)
+    assert np.array_equal(idx, idx_tc) and np.allclose(w, w_tc, atol=1e-15)
+    # M_core >= number of experts with a vote, K >= k: the same as token choice
+    n_voted = np.unique(orc.tc_select(L, k)).size
+    _, core = orc.des_vote(L, P, k, n_voted)
+    idx, w = orc.core_reroute(L, P, core, k, True)
+    assert np.array_equal(idx, idx_tc)
+    # a smaller core changes the routing and keeps every slot inside the core
+    _, core = orc.des_vote(L, P, k, 16)
+    idx, _ = orc.core_reroute(L, P, core, k, True)
+    assert np.isin(idx, core).all() and np.unique(idx).size <= 16
+
+
+def test_des_core_smaller_than_k():
+    rng = np.random.default_rng(8)
+    L = rng.standard_normal((5, 12))
+    _, core = orc.des_vote(L, orc.softmax(L), 8, 3)
+    idx, w = orc.core_reroute(L, orc.softmax(L), core, 8, True)
+    assert idx.shape == (5, 3) and np.allclose(w.sum(1), 1.0)
+
+
+def test_des_seq_is_union_of_topk():
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((6, 20))
+    core = orc.des_seq_core(L, 2)
+    want = sorted({e for s in range(6) for e in _brute_topk(L[s], 2)})
+    assert list(core) == want
+
+
+def test_des_latency_model():
+    # f(c) = a c + b for c > 0: two experts with 3 and 5 tokens, one idle.
+    assert orc.des_block_latency([3, 0, 5], a=2.0, b=10.0) == (2 * 3 + 10) + (2 * 5 + 10)
+
+
+# ------------------------------------------------------------------------------ permutation
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_counting_sort_properties(seed):
+    rng = np.random.default_rng(30 + seed)
+    S, E, k = 97, 11, 3
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(S)])
+    valid = rng.random((S, k)) > 0.2
+    counts, offsets, row_token, row_slot, token_rows = orc.counting_sort(idx, E, valid)
+    assert np.array_equal(offsets[1:] - offsets[:-1], counts)
+    assert offsets[0] == 0 and offsets[-1] == valid.sum()
+    # brute force grouping
+    want = [(e, s, j) for e in range(E) for s in range(S) for j in range(k) if valid[s, j] and idx[s, j] == e]
+    assert [(int(idx[s, j]), int(s), int(j)) for s, j in zip(row_token, row_slot)] == want
+    for s in range(S):
+        for j in range(k):
+            r = token_rows[s, j]
+            if valid[s, j]:
+                assert row_token[r] == s and row_slot[r] == j
+            else:
+                assert r == -1
+
+
+# ------------------------------------------------------------------------------ experts
+
+
+def test_gelu_matches_normal_cdf_table():
+    g = _gold("normal_cdf.json")
+    for z, phi in g["values"]:
+        assert abs(orc.gelu(z) - z * phi) <= abs(z) * g["tolerance"] + 1e-15
+
+
+def test_silu_matches_logistic():
+    g = _gold("logistic.json")
+    for z, sig in g["values"]:
+        assert abs(orc.silu(z) - z * sig) <= g["tolerance"]
+
+
+def test_gelu_tanh_close_to_erf_form():
+    z = np.linspace(-4, 4, 81)
+    assert np.max(np.abs(orc.gelu_tanh(z) - orc.gelu(z))) < 1e-3
+
+
+def test_mlp_hand_worked():
+    """d=2, f=3, GELU. x=(1,2). W1 rows (1,0), (-1,0), (2,-1) give pre-activations (1,-1,0);
+    gelu = (Phi(1), -Phi(-1), 0). W2 = [[1,2,3],[0,-1,4]] then gives
+    y = (Phi(1) - 2 Phi(-1), Phi(-1))."""
+    phi = dict((z, p) for z, p in _gold("normal_cdf.json")["values"])
+    x = np.array([[1.0, 2.0]])
+    w1 = np.array([[1.0, 0.0], [-1.0, 0.0], [2.0, -1.0]])
+    w2 = np.array([[1.0, 2.0, 3.0], [0.0, -1.0, 4.0]])
+    y = orc.mlp(x, w1, None, w2, "gelu")
+    assert np.allclose(y, [[phi[1.0] - 2 * phi[-1.0], phi[-1.0]]], atol=1e-10)
+    # SwiGLU: gate rows (1,0),(0,1) -> (1,2); up rows (0,1),(1,1) -> (2,3);
+    # h = (silu(1)*2, silu(2)*3) = (2 sigma(1), 6 sigma(2)); W2 = [[1,-1]] -> y = 2 sigma(1) - 6 sigma(2)
+    sig = dict((z, p) for z, p in _gold("logistic.json")["values"])
+    w3 = np.array([[1.0, 0.0], [0.0, 1.0]])
+    w1 = np.array([[0.0, 1.0], [1.0, 1.0]])
+    y = orc.mlp(x, w1, w3, np.array([[1.0, -1.0]]), "swiglu")
+    assert abs(y[0, 0] - (2 * sig[1.0] - 6 * sig[2.0])) < 1e-12
+
+
+def _light_spec(**kw):
+    base = dict(name="light", S=40, d=16, f=8, E_heavy=2, n_identity=1, n_zero=1, n_const=1,
+                act="gelu", mode="tc", k=1, renorm=True, dtype="f32")
+    base.update(kw)
+    return LayerSpec(**base)
+
+
+def test_zero_and_identity_and_const_experts():
+    spec = _light_spec()
+    W = gen_layer_inputs(spec, seed=3)
+    S, E = spec.S, spec.E_routed
+    L = np.zeros((S, E))
+    for target, kind in ((3, "zero"), (2, "identity"), (4, "const")):
+        Lt = L.copy()
+        Lt[:, target] = 5.0
+        rt = orc.route(spec, L=Lt)
+        assert np.all(rt["idx"][:, 0] == target) and np.all(rt["w"] == 1.0)
+        r = orc.layer_forward(spec, W, W.x, rt=rt)
+        if kind == "zero":
+            assert np.all(r["y"] == 0.0)
+        elif kind == "identity":
+            assert np.array_equal(r["y"], W.x.astype(float))
+        else:
+            assert np.array_equal(r["y"], np.broadcast_to(W.const_vec[0][0].astype(float), (S, spec.d)))
+    # top-2 without renorm: constant expert with weight g gives g * v_c
+    spec2 = _light_spec(k=2, renorm=False)
+    Lt = np.zeros((S, E))
+    Lt[:, 4] = 3.0
+    Lt[:, 3] = 2.0                                  # the zero expert takes the second slot
+    rt = orc.route(spec2, L=Lt)
+    r = orc.layer_forward(spec2, W, W.x, rt=rt)
+    g = orc.softmax(Lt)[:, 4]
+    assert np.allclose(r["y"], g[:, None] * W.const_vec[0][0][None, :].astype(float), atol=1e-15)
+
+
+def test_combine_sensitivity_identity():
+    """d||y|| / d h^e = s^e * y / ||y|| for y = sum_e s^e h^e (DICE, conditional communication)."""
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((3, 10))           # three expert outputs for one token
+    s = np.array([0.5, 0.3, 0.2])
+
+    def ynorm(hh):
+        return np.linalg.norm((s[:, None] * hh).sum(0))
+
+    y = (s[:, None] * h).sum(0)
+    eps = 1e-6
+    for e in range(3):
+        for i in range(10):
+            hp, hm = h.copy(), h.copy()
+            hp[e, i] += eps
+            hm[e, i] -= eps
+            fd = (ynorm(hp) - ynorm(hm)) / (2 * eps)
+            assert abs(fd - s[e] * y[i] / np.linalg.norm(y)) < 1e-8
+
+
+# ------------------------------------------------------------------------------ layer-level
+
+
+def test_dice_reuse_extremes():
+    spec = _light_spec(E_heavy=4, n_identity=0, n_zero=0, n_const=0, n_shared=1, k=2, reuse_tau=0.0)
+    W = gen_layer_inputs(spec, seed=4, std=0.2)
+    cache = np.random.default_rng(5).standard_normal((spec.S, spec.d))
+    base = orc.layer_forward(spec, W, W.x, cache=cache)
+    assert not base["rt"]["reuse"].any()
+    # tau > 1: every token reuses, routed part == cache exactly, nothing dispatched
+    spec_all = spec.replace(reuse_tau=1.5)
+    r = orc.layer_forward(spec_all, W, W.x, cache=cache)
+    assert r["rt"]["reuse"].all()
+    assert np.array_equal(r["routed"], cache)
+    assert np.allclose(r["y"] - orc.shared_out(spec, W, 0, W.x), cache, atol=1e-14)
+    valid = ~np.broadcast_to(r["rt"]["reuse"][:, None], r["rt"]["idx"].shape)
+    assert orc.counting_sort(r["rt"]["idx"], spec.E_routed, valid)[0].sum() == 0
+
+
+def test_gate_residual_with_zero_router_keeps_routing():
+    spec = _light_spec(n_identity=0, n_zero=0, n_const=0, E_heavy=6, k=2, n_layers=3)
+    W = gen_layer_inputs(spec, seed=6, std=0.3)
+    for layer in range(1, spec.n_layers):
+        W.w_router[layer][:] = 0.0
+    outs = orc.stack_forward(spec, W, W.x, act_bf16=False)
+    for r in outs[1:]:
+        assert np.array_equal(r["rt"]["idx"], outs[0]["rt"]["idx"])
+        assert np.allclose(r["logits"], outs[0]["logits"], atol=0)
+    # and the residual stream adds each layer's output
+    assert np.allclose(outs[1]["h_in"], outs[0]["y"])
+
+
+def test_bf16_round_reference_values():
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: ties to even -> 1.0; just above rounds up.
+    assert orc.bf16_round(1.0 + 2 ** -8) == 1.0
+    assert orc.bf16_round(1.0 + 2 ** -8 + 2 ** -12) == 1.0 + 2 ** -7
+    assert orc.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6     # tie -> even mantissa
+    assert orc.bf16_round(-3.0) == -3.0
