@@ -1,0 +1,282 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+Default workload: the DiT-MoE-XL-shaped layer (32 x 256 = 8192 tokens, d=1152, 8 SwiGLU experts
+1152->4608->1152 + 2 shared experts, top-2 renormalised), bf16, seeded synthetic inputs. A step is
+one moe_layer_forward call: router GEMM, softmax + top-k, counting-sort dispatch, the grouped expert
+GEMMs (gather fused) and the combine. Inputs are resident in HBM before timing starts.
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (its duration read live with
+HIP events attached to its launches on its own stream), and the fp64 CPU oracle timed on a bounded
+sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (GEMM) / % HBM peak (routing, DES)"
+
+DESCRIPTIONS = {
+    "dit_moe_tiny_f32": "1 x 256 tokens, d=384, 8 GELU experts 384->1536->384, top-2 renormalised, fp32",
+    "dit_moe_xl": "32 x 256 = 8192 tokens, d=1152, 8 SwiGLU experts 1152->4608->1152 + 2 shared, top-2 renormalised",
+    "dit_moe_xl_reuse": "dit_moe_xl with cached routed outputs reused for tokens whose top softmax score < 0.3",
+    "ec_dit": "64 x 128 = 8192 tokens, d=1536, 32 GELU experts 1536->6144->1536, expert choice C=512",
+    "des_vote_b025": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 16",
+    "des_vote_b050": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 32",
+    "mmoe": "MMOE MoE++ stack: 64 x 256 = 16384 tokens, d=1152, 16 GELU experts + identity/zero/constant + 1 shared, "
+            "top-2 with gate residual, 4 layers",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="dit_moe_xl", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
+    return ap.parse_args()
+
+
+def sha256_of(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it was taken on the current
+    kernel source; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    m_file = re.search(r"source_file:\s*(\S+)", txt)
+    if not (m_src and m_b and m_file):
+        return None
+    if sha256_of(os.path.join(ROOT, m_file.group(1))) != m_src.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_gemm_amd as moe
+    from synth import WORKLOADS, gen_layer_inputs, gen_tensor
+
+    spec = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if spec.dtype == "bf16" else torch.float32
+
+    def up(vals, bits):
+        if bits is None:
+            return torch.from_numpy(np.ascontiguousarray(vals, np.float32)).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    t0 = time.time()
+    inp = gen_layer_inputs(spec, seed=0)
+    x = up(inp.x, inp.bits.get("x"))
+    copies = 4 if spec.mode == "des" else 1      # rotate weight copies so the 256 MB MALL cannot hold them
+    layers = []
+    for layer in range(spec.n_layers):
+        per_copy = []
+        for c in range(copies):
+            b = inp.bits
+            t = {"w_router": up(inp.w_router[layer], b.get(f"w_router.{layer}"))}
+            if spec.E_heavy:
+                t["w1"] = up(inp.w1[layer], b.get(f"w1.{layer}"))
+                t["w2"] = up(inp.w2[layer], b.get(f"w2.{layer}"))
+                if inp.w3[layer] is not None:
+                    t["w3"] = up(inp.w3[layer], b.get(f"w3.{layer}"))
+            if spec.n_shared:
+                t["s_w1"] = up(inp.s_w1[layer], b.get(f"s_w1.{layer}"))
+                t["s_w2"] = up(inp.s_w2[layer], b.get(f"s_w2.{layer}"))
+                if inp.s_w3[layer] is not None:
+                    t["s_w3"] = up(inp.s_w3[layer], b.get(f"s_w3.{layer}"))
+            if spec.n_const:
+                t["const_vec"] = up(inp.const_vec[layer], b.get(f"const_vec.{layer}"))
+            per_copy.append((t, moe.weights_struct(t)))
+        layers.append(per_copy)
+    desc = moe.desc_from_spec(spec)
+    ws = moe.workspace(desc, device=dev)
+    rb = moe.alloc_routing(desc, device=dev)
+    stream = torch.cuda.current_stream()
+    cache = None
+    if spec.reuse_tau > 0:
+        # the cache holds the routed part of a previous call on slightly different tokens
+        xv, xb = gen_tensor(np.random.default_rng(1), (spec.S, spec.d), 0.05, spec.dtype)
+        x_prev = up(np.asarray(inp.x, np.float32) + xv, None).to(dt)
+        cache = torch.zeros((spec.S, spec.d), dtype=dt, device=dev)
+        d0 = moe.desc_from_spec(spec.replace(reuse_tau=0.0))
+        ws0 = moe.workspace(d0, device=dev)
+        y0 = torch.empty_like(x)
+        moe.moe_layer_forward(d0, x_prev, layers[0][0][1], None, None, None, cache, None, y0, ws0)
+        torch.cuda.synchronize()
+    hs = [torch.empty_like(x) for _ in range(spec.n_layers)]
+    logits = [torch.empty((spec.S, spec.E_routed), dtype=torch.float32, device=dev) for _ in range(spec.n_layers)]
+    setup_s = time.time() - t0
+
+    def step(i):
+        h = x
+        prev = None
+        for layer in range(spec.n_layers):
+            w = layers[layer][i % copies][1]
+            res = h if spec.n_layers > 1 else None
+            moe.moe_layer_forward(desc, h, w, prev, logits[layer] if spec.n_layers > 1 else None,
+                                  rb.struct if layer == spec.n_layers - 1 else None, cache, res, hs[layer], ws,
+                                  stream=stream.cuda_stream)
+            h = hs[layer]
+            prev = logits[layer]
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel times: a second pass with event pairs attached to every launch
+    moe.moe_profile_begin()
+    for i in range(args.steps):
+        step(i)
+    prof = moe.moe_profile_end()
+    torch.cuda.synchronize()
+    kernels = {k: {"avg_us": round(v[0] * 1e3 / v[1], 2), "launches": v[1]} for k, v in prof.items()}
+
+    # algorithmic work per launch from the actual routing
+    n_rows = int(rb["n_rows"][0].item())
+    counts = rb["counts"].cpu().numpy()
+    n_active = int(np.count_nonzero(counts[: spec.E_heavy])) if spec.E_heavy else 0
+    d, f = spec.d, spec.f
+    mats_up = 2 if spec.act == "swiglu" else 1
+    rows_gemm = n_rows + spec.S * spec.n_shared
+    work = {
+        "gemm_up": ("mfma", rows_gemm * 2.0 * d * f * mats_up),
+        "gemm_down": ("mfma", rows_gemm * 2.0 * d * f),
+        "stream_up": ("hbm", n_active * mats_up * f * d * (2 if spec.dtype == "bf16" else 4)),
+        "stream_down": ("hbm", n_active * d * f * (2 if spec.dtype == "bf16" else 4)),
+    }
+    if spec.mode == "des" or (spec.E_heavy and desc and n_rows and spec.S * spec.k / max(1, spec.E_heavy) <= 64):
+        # streamed experts: the shared experts (if any) still run on the tiled GEMM
+        work["gemm_up"] = ("mfma", spec.S * spec.n_shared * 2.0 * d * f * mats_up)
+        work["gemm_down"] = ("mfma", spec.S * spec.n_shared * 2.0 * d * f)
+    cand = [k for k in work if k in prof and work[k][1] > 0]
+    dom = max(cand, key=lambda k: prof[k][0]) if cand else None
+    roofline = None
+    if dom:
+        avg_s = prof[dom][0] / prof[dom][1] / 1e3
+        bound, amount = work[dom]
+        if bound == "mfma":
+            peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+            achieved = amount / avg_s / 1e12
+            unit = "TFLOP/s"
+        else:
+            peak = PEAK_HBM_GBS
+            achieved = amount / avg_s / 1e9
+            unit = "GB/s"
+        roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                    "frac": round(achieved / peak, 4), "traffic": read_traffic(dom, args.workload),
+                    "work_per_launch": amount, "avg_us": round(avg_s * 1e6, 2)}
+
+    layer_flops = spec.n_layers * (2.0 * spec.S * d * spec.E_routed + rows_gemm * 2.0 * d * f * (mats_up + 1))
+    tokens_per_s = spec.S / (ms / 1e3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(spec, inp, args.cpu_tokens)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights)",
+        "config": {"workload": f"{args.workload}: {DESCRIPTIONS[args.workload]}", "tokens_per_step": spec.S,
+                   "layers": spec.n_layers, "dispatched_rows": n_rows, "active_experts": n_active},
+        "layer_tflops": round(layer_flops / (ms / 1e3) / 1e12, 2),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, inp, n_tokens):
+    """The fp64 oracle, untuned, on the first n tokens of the same inputs (bounded so the run stays
+    around 10-30 s). Token choice and DES routing of a token do not depend on other tokens of the
+    sample; for expert choice the sample is routed on its own."""
+    import numpy as np
+
+    import oracle as orc
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = os.cpu_count()
+
+    def run(n):
+        sub = spec.replace(S=n)
+        x = inp.x[:n].astype(np.float64)
+        t = time.perf_counter()
+        h, prev = x, None
+        for layer in range(spec.n_layers):
+            r = orc.layer_forward(sub, inp, h, layer=layer, prev_logits=prev,
+                                  cache=np.zeros_like(x) if spec.reuse_tau > 0 else None,
+                                  residual=h if spec.n_layers > 1 else None)
+            h, prev = r["y"], r["logits"]
+        return time.perf_counter() - t
+
+    if n_tokens <= 0:
+        n0 = min(spec.S, 128)
+        t0 = run(n0)
+        n_tokens = int(min(spec.S, max(n0, n0 * 12.0 / max(t0, 1e-3))))
+    n_tokens = min(n_tokens, spec.S)
+    t = run(n_tokens)
+    return {"value": round(n_tokens / t, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {spec.S} tokens, whole layer ({spec.n_layers} layer(s)), numpy fp64",
+            "seconds": round(t, 2)}
+
+
+if __name__ == "__main__":
+    main()

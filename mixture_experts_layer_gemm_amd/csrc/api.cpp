@@ -1,0 +1,604 @@
+// C ABI of the MoE layer library: argument validation, workspace plan and launch sequence.
+// The operations and their sources are described in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "moe.h"
+
+// ---------------------------------------------------------------------------------------------
+// Launch profiling: a fixed pool of events, handed out in launch order while enabled.
+namespace moe {
+namespace prof {
+struct Rec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+struct Entry {
+  std::string name;
+  double ms;
+  int32_t launches;
+};
+static bool g_on = false;
+static std::vector<hipEvent_t> g_pool;
+static std::vector<Rec> g_recs;
+static std::vector<Entry> g_entries;
+constexpr size_t kPoolPairs = 4096;
+
+bool enabled() { return g_on; }
+
+bool take(const char* name, hipEvent_t* start, hipEvent_t* stop) {
+  const size_t n = g_recs.size();
+  if (2 * n + 2 > g_pool.size()) return false;
+  *start = g_pool[2 * n];
+  *stop = g_pool[2 * n + 1];
+  g_recs.push_back({name, *start, *stop});
+  return true;
+}
+}  // namespace prof
+}  // namespace moe
+
+namespace {
+
+using namespace moe;
+
+constexpr uint32_t kKnownFlags = MOE_F_INPUT_PROBS | MOE_F_SYNC_DEBUG | MOE_F_FORCE_TILED | MOE_F_FORCE_STREAM;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxK = 16;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Everything derived from a validated descriptor.
+struct Plan {
+  int E_r = 0, k_eff = 0, C = 0;
+  int64_t R_max = 0;
+  bool streaming = false;     // heavy experts on the weight-streaming kernel
+  size_t esz = 0;             // element size of dtype
+  // workspace pieces (byte offsets)
+  size_t o_blk = 0, o_filt = 0, o_pT = 0, o_mask = 0, o_tokrows = 0;   // route scratch
+  size_t o_logits = 0;                                                  // router output
+  size_t o_rt = 0;                                                      // internal routing arrays
+  size_t o_h = 0, o_hs = 0, o_yp = 0, o_ys = 0;                         // expert buffers
+  size_t total = 0;
+  // internal routing array offsets (relative to o_rt)
+  size_t r_idx = 0, r_w = 0, r_cnt = 0, r_off = 0, r_rtok = 0, r_rw = 0, r_trow = 0, r_toff = 0, r_tlist = 0,
+         r_core = 0, r_votes = 0, r_reuse = 0, r_nrows = 0, r_cap = 0, r_size = 0;
+};
+
+bool finite_nonneg(float v) { return std::isfinite(v) && v >= 0.f; }
+
+moe_status make_plan(const moe_desc* d, Plan* p) {
+  if (!d) return MOE_EINVAL;
+  if (d->flags & ~kKnownFlags) return MOE_EINVAL;
+  if (d->S < 1 || d->d < 1 || d->E_heavy < 0 || d->n_identity < 0 || d->n_zero < 0 || d->n_const < 0 ||
+      d->n_shared < 0)
+    return MOE_EINVAL;
+  if (d->dtype != MOE_BF16 && d->dtype != MOE_F32) return MOE_EINVAL;
+  if (d->act != MOE_ACT_GELU && d->act != MOE_ACT_GELU_TANH && d->act != MOE_ACT_SWIGLU) return MOE_EINVAL;
+  if (d->mode != MOE_TOKEN_CHOICE && d->mode != MOE_EXPERT_CHOICE && d->mode != MOE_DES_VOTE) return MOE_EINVAL;
+  const int64_t E_r = (int64_t)d->E_heavy + d->n_identity + d->n_zero + d->n_const;
+  if (E_r < 1) return MOE_EINVAL;
+  if ((d->E_heavy > 0 || d->n_shared > 0) && d->d_ff < 1) return MOE_EINVAL;
+  if (!finite_nonneg(d->reuse_tau)) return MOE_EINVAL;
+  if ((d->flags & MOE_F_FORCE_TILED) && (d->flags & MOE_F_FORCE_STREAM)) return MOE_EINVAL;
+  p->E_r = (int)std::min<int64_t>(E_r, 1 << 30);
+  p->esz = d->dtype == MOE_BF16 ? 2 : 4;
+  if (d->mode == MOE_EXPERT_CHOICE) {
+    if (!std::isfinite(d->capacity_factor) || d->capacity_factor <= 0.f) return MOE_EINVAL;
+    const double c = std::floor((double)d->capacity_factor * (double)d->S / (double)E_r);
+    const int64_t C = (int64_t)std::min<double>((double)d->S, c);
+    if (C < 1) return MOE_EINVAL;
+    p->C = (int)C;
+    p->k_eff = 0;
+    p->R_max = E_r * C;
+  } else {
+    if (d->k < 1 || d->k > E_r) return MOE_EINVAL;
+    p->k_eff = d->k;
+    if (d->mode == MOE_DES_VOTE) {
+      if (d->m_core < 1 || d->m_core > E_r || d->vote_k < 1 || d->vote_k > E_r) return MOE_EINVAL;
+      p->k_eff = std::min(d->k, d->m_core);
+    }
+    p->R_max = (int64_t)d->S * p->k_eff;
+  }
+  // What this library implements.
+  if (E_r > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (p->k_eff > kMaxK) return MOE_EUNSUPPORTED;
+  if (d->mode == MOE_EXPERT_CHOICE && (d->n_identity + d->n_zero + d->n_const > 0 || d->reuse_tau > 0.f))
+    return MOE_EUNSUPPORTED;
+  if (d->d % 8 != 0) return MOE_EUNSUPPORTED;
+  if (d->d % (d->dtype == MOE_BF16 ? 32 : 16) != 0) return MOE_EUNSUPPORTED;   // router MFMA steps
+  // kernels index rows of x, H and y_perm with 32-bit element offsets
+  const int64_t lim = ((int64_t)1 << 31) - 1;
+  const int64_t ff = std::max(d->d_ff, 0);
+  if ((int64_t)d->S * E_r > lim || p->R_max > lim || (int64_t)d->S * d->d > lim || p->R_max * ff > lim ||
+      p->R_max * d->d > lim || (int64_t)d->S * d->n_shared * ff > lim || ff * d->d > lim)
+    return MOE_EUNSUPPORTED;
+  const int act = d->act;
+  if (d->E_heavy > 0) {
+    const int64_t per_expert = p->R_max / std::max<int64_t>(1, std::min<int64_t>(
+                                                                   d->E_heavy, d->mode == MOE_DES_VOTE ? d->m_core : d->E_heavy));
+    bool stream = per_expert <= 64;
+    if (d->flags & MOE_F_FORCE_TILED) stream = false;
+    if (d->flags & MOE_F_FORCE_STREAM) stream = true;
+    p->streaming = stream;
+    if (stream) {
+      if (!stream_gemm_supported(d->dtype, GEMM_UP, act, d->d_ff, d->d) ||
+          !stream_gemm_supported(d->dtype, GEMM_DOWN, act, d->d, d->d_ff))
+        return MOE_EUNSUPPORTED;
+    } else {
+      if (!grouped_gemm_supported(d->dtype, GEMM_UP, act, d->d_ff, d->d) ||
+          !grouped_gemm_supported(d->dtype, GEMM_DOWN, act, d->d, d->d_ff))
+        return MOE_EUNSUPPORTED;
+    }
+  }
+  if (d->n_shared > 0) {
+    if (!grouped_gemm_supported(d->dtype, GEMM_UP, act, d->d_ff, d->d) ||
+        !grouped_gemm_supported(d->dtype, GEMM_DOWN, act, d->d, (int)std::min<int64_t>((int64_t)d->n_shared * d->d_ff, 1 << 30)))
+      return MOE_EUNSUPPORTED;
+  }
+
+  // ---- workspace plan
+  const size_t S = (size_t)d->S, Er = (size_t)E_r, R = (size_t)p->R_max;
+  const size_t k = (size_t)std::max(p->k_eff, 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const int nblk = permute_num_blocks(d->S, std::max(p->k_eff, 1));
+  p->o_blk = take((size_t)nblk * std::max(d->E_heavy, 1) * 4);
+  p->o_filt = take(d->mode == MOE_DES_VOTE ? S * Er * 4 : 0);
+  p->o_pT = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
+  p->o_mask = take(d->mode == MOE_EXPERT_CHOICE ? S * ((Er + 31) / 32) * 4 : 0);
+  p->o_tokrows = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
+  p->o_logits = take(S * Er * 4);
+  // internal routing arrays
+  size_t r = 0;
+  auto rt = [&](size_t bytes) {
+    const size_t o = r;
+    r += align256(bytes);
+    return o;
+  };
+  p->r_idx = rt(S * k * 4);
+  p->r_w = rt(S * k * 4);
+  p->r_cnt = rt(Er * 4);
+  p->r_off = rt((Er + 1) * 4);
+  p->r_rtok = rt(R * 4);
+  p->r_rw = rt(R * 4);
+  p->r_trow = rt(S * k * 4);
+  p->r_toff = rt((S + 1) * 4);
+  p->r_tlist = rt(R * 4);
+  p->r_core = rt((size_t)std::max(d->m_core, 1) * 4);
+  p->r_votes = rt(Er * 4);
+  p->r_reuse = rt(S);
+  p->r_nrows = rt(4);
+  p->r_cap = rt(4);
+  p->r_size = r;
+  p->o_rt = take(r);
+  const size_t f = (size_t)std::max(d->d_ff, 0);
+  p->o_h = take(d->E_heavy > 0 ? R * f * p->esz : 0);
+  p->o_hs = take(S * (size_t)d->n_shared * f * p->esz);
+  p->o_yp = take(d->E_heavy > 0 ? R * (size_t)d->d * 4 : 0);
+  p->o_ys = take(d->n_shared > 0 ? S * (size_t)d->d * 4 : 0);
+  p->total = std::max<size_t>(off, 256);
+  return MOE_OK;
+}
+
+moe_status check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return MOE_EWORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return MOE_EWORKSPACE;
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+moe_status after_launch(hipError_t e, const moe_desc* d, hipStream_t st) {
+  if (e != hipSuccess) return MOE_EHIP;
+  if (d->flags & MOE_F_SYNC_DEBUG) {
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_EHIP;
+    if (hipGetLastError() != hipSuccess) return MOE_EHIP;
+  }
+  return MOE_OK;
+}
+
+#define MOE_TRY(expr)                   \
+  do {                                  \
+    const moe_status _s = (expr);       \
+    if (_s != MOE_OK) return _s;        \
+  } while (0)
+
+moe_status check_routing(const moe_desc* d, const moe_routing* r) {
+  if (!r) return MOE_EINVAL;
+  if (!r->counts || !r->offsets || !r->row_token || !r->row_w || !r->n_rows) return MOE_EINVAL;
+  if (d->mode == MOE_EXPERT_CHOICE) {
+    if (!r->token_off || !r->token_list) return MOE_EINVAL;
+  } else {
+    if (!r->topk_idx || !r->topk_w || !r->token_rows) return MOE_EINVAL;
+    if (d->reuse_tau > 0.f && !r->reuse) return MOE_EINVAL;
+    if (d->mode == MOE_DES_VOTE && (!r->core || !r->votes)) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
+moe_routing internal_routing(const Plan& p, const moe_desc* d, void* ws) {
+  uint8_t* b = (uint8_t*)ws + p.o_rt;
+  moe_routing r{};
+  r.topk_idx = (int32_t*)(b + p.r_idx);
+  r.topk_w = (float*)(b + p.r_w);
+  r.probs = nullptr;
+  r.counts = (int32_t*)(b + p.r_cnt);
+  r.offsets = (int32_t*)(b + p.r_off);
+  r.row_token = (int32_t*)(b + p.r_rtok);
+  r.row_w = (float*)(b + p.r_rw);
+  r.token_rows = (int32_t*)(b + p.r_trow);
+  r.token_off = (int32_t*)(b + p.r_toff);
+  r.token_list = (int32_t*)(b + p.r_tlist);
+  r.core = (int32_t*)(b + p.r_core);
+  r.votes = (float*)(b + p.r_votes);
+  r.reuse = d->reuse_tau > 0.f ? (uint8_t*)(b + p.r_reuse) : nullptr;
+  r.n_rows = (int32_t*)(b + p.r_nrows);
+  r.capacity = (int32_t*)(b + p.r_cap);
+  return r;
+}
+
+moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool input_probs, const moe_routing* r,
+                    void* ws, hipStream_t st) {
+  uint8_t* w = (uint8_t*)ws;
+  if (d->mode == MOE_EXPERT_CHOICE) {
+    ECArgs a{};
+    a.S = d->S;
+    a.E = p.E_r;
+    a.C = p.C;
+    a.input_probs = input_probs;
+    a.keys = keys;
+    a.probs = r->probs;
+    a.pT = (float*)(w + p.o_pT);
+    a.tok_mask = (uint32_t*)(w + p.o_mask);
+    a.tok_rows_tmp = (int32_t*)(w + p.o_tokrows);
+    a.counts = r->counts;
+    a.offsets = r->offsets;
+    a.row_token = r->row_token;
+    a.row_w = r->row_w;
+    a.token_off = r->token_off;
+    a.token_list = r->token_list;
+    a.n_rows = r->n_rows;
+    a.capacity = r->capacity;
+    return after_launch(launch_route_ec(a, st), d, st);
+  }
+  RouteArgs a{};
+  a.S = d->S;
+  a.E_r = p.E_r;
+  a.E_heavy = d->E_heavy;
+  a.k = p.k_eff;
+  a.renorm = d->renorm != 0;
+  a.input_probs = input_probs;
+  a.n_identity = d->n_identity;
+  a.n_zero = d->n_zero;
+  a.n_const = d->n_const;
+  a.tau = d->reuse_tau;
+  a.vote_k = d->vote_k;
+  a.m_core = d->m_core;
+  a.keys = keys;
+  a.probs = r->probs;
+  a.topk_idx = r->topk_idx;
+  a.topk_w = r->topk_w;
+  a.reuse = r->reuse;
+  a.votes = r->votes;
+  a.core = r->core;
+  if (d->mode == MOE_DES_VOTE) {
+    a.k = d->k;   // the kernel applies min(k, m_core)
+    MOE_TRY(after_launch(launch_route_des(a, (float*)(w + p.o_filt), st), d, st));
+  } else {
+    MOE_TRY(after_launch(launch_route_topk(a, st), d, st));
+  }
+  PermuteArgs q{};
+  q.S = d->S;
+  q.k = p.k_eff;
+  q.E_r = p.E_r;
+  q.E_heavy = d->E_heavy;
+  q.topk_idx = r->topk_idx;
+  q.topk_w = r->topk_w;
+  q.reuse = d->reuse_tau > 0.f ? r->reuse : nullptr;
+  q.counts = r->counts;
+  q.offsets = r->offsets;
+  q.row_token = r->row_token;
+  q.row_w = r->row_w;
+  q.token_rows = r->token_rows;
+  q.n_rows = r->n_rows;
+  q.blk_cnt = (int32_t*)(w + p.o_blk);
+  return after_launch(launch_permute(q, st), d, st);
+}
+
+moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const void* x_perm, const moe_routing* r,
+                      const moe_weights* wt, float* y_perm, float* y_shared, void* ws, hipStream_t st) {
+  uint8_t* w = (uint8_t*)ws;
+  const int64_t f = d->d_ff, dm = d->d;
+  void* H = w + p.o_h;
+  void* Hs = w + p.o_hs;
+  GemmProblem up[2], dn[2];
+  int64_t ub[2];
+  int nup = 0;
+  if (d->E_heavy > 0) {
+    GemmProblem u{};
+    u.A = x_perm ? x_perm : x;
+    u.a_rows = x_perm ? nullptr : r->row_token;
+    u.lda = dm;
+    u.B = wt->w1;
+    u.B3 = wt->w3;
+    u.ldb = dm;
+    u.b_gstride = f * dm;
+    u.k_seg = dm;
+    u.k_seg_stride = 0;
+    u.C = H;
+    u.ldc = f;
+    u.c_gcol = 0;
+    u.offsets = r->offsets;
+    u.G = d->E_heavy;
+    u.M_uni = 0;
+    u.N = (int32_t)f;
+    u.K = (int32_t)dm;
+    GemmProblem v = u;
+    v.A = H;
+    v.a_rows = nullptr;
+    v.lda = f;
+    v.B = wt->w2;
+    v.B3 = nullptr;
+    v.ldb = f;
+    v.b_gstride = dm * f;
+    v.k_seg = f;
+    v.C = y_perm;
+    v.ldc = dm;
+    v.N = (int32_t)dm;
+    v.K = (int32_t)f;
+    if (p.streaming) {
+      const int max_active = (int)std::min<int64_t>(
+          {(int64_t)d->E_heavy, p.R_max, d->mode == MOE_DES_VOTE ? (int64_t)d->m_core : (int64_t)d->E_heavy});
+      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_UP, d->act, u, max_active, st), d, st));
+      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_DOWN, d->act, v, max_active, st), d, st));
+    } else {
+      up[nup] = u;
+      dn[nup] = v;
+      ub[nup] = p.R_max;
+      ++nup;
+    }
+  }
+  if (d->n_shared > 0) {
+    const int64_t ns = d->n_shared;
+    GemmProblem u{};
+    u.A = x;
+    u.a_rows = nullptr;
+    u.lda = dm;
+    u.B = wt->s_w1;
+    u.B3 = wt->s_w3;
+    u.ldb = dm;
+    u.b_gstride = f * dm;
+    u.k_seg = dm;
+    u.k_seg_stride = 0;
+    u.C = Hs;
+    u.ldc = ns * f;
+    u.c_gcol = f;
+    u.offsets = nullptr;
+    u.G = (int32_t)ns;
+    u.M_uni = d->S;
+    u.N = (int32_t)f;
+    u.K = (int32_t)dm;
+    // down: one GEMM over the K-concatenation [H_1 | ... | H_ns] . [W2_1 | ... | W2_ns]^T
+    GemmProblem v{};
+    v.A = Hs;
+    v.a_rows = nullptr;
+    v.lda = ns * f;
+    v.B = wt->s_w2;
+    v.B3 = nullptr;
+    v.ldb = f;
+    v.b_gstride = 0;
+    v.k_seg = f;
+    v.k_seg_stride = dm * f;
+    v.C = y_shared;
+    v.ldc = dm;
+    v.c_gcol = 0;
+    v.offsets = nullptr;
+    v.G = 1;
+    v.M_uni = d->S;
+    v.N = (int32_t)dm;
+    v.K = (int32_t)(ns * f);
+    up[nup] = u;
+    dn[nup] = v;
+    ub[nup] = d->S;
+    ++nup;
+  }
+  if (nup > 0) {
+    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_UP, d->act, up, ub, nup, st), d, st));
+    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_DOWN, d->act, dn, ub, nup, st), d, st));
+  }
+  return MOE_OK;
+}
+
+moe_status do_combine(const moe_desc* d, const Plan& p, const void* x, const moe_routing* r, const float* y_perm,
+                      const float* y_shared, const void* const_vec, void* cache, const void* residual, void* y,
+                      hipStream_t st) {
+  CombineArgs a{};
+  a.dtype = d->dtype;
+  a.mode = d->mode == MOE_EXPERT_CHOICE ? 1 : 0;
+  a.S = d->S;
+  a.d = d->d;
+  a.k = p.k_eff;
+  a.E_heavy = d->E_heavy;
+  a.n_identity = d->n_identity;
+  a.n_zero = d->n_zero;
+  a.n_const = d->n_const;
+  a.x = x;
+  a.topk_idx = r->topk_idx;
+  a.topk_w = r->topk_w;
+  a.token_rows = r->token_rows;
+  a.token_off = r->token_off;
+  a.token_list = r->token_list;
+  a.row_w = r->row_w;
+  a.reuse = d->reuse_tau > 0.f ? r->reuse : nullptr;
+  a.y_perm = y_perm;
+  a.y_shared = d->n_shared > 0 ? y_shared : nullptr;
+  a.const_vec = const_vec;
+  a.cache = cache;
+  a.residual = residual;
+  a.y = y;
+  return after_launch(launch_combine(a, st), d, st);
+}
+
+moe_status check_weights(const moe_desc* d, const moe_weights* w, bool need_router) {
+  if (!w) return MOE_EINVAL;
+  if (need_router && !w->w_router) return MOE_EINVAL;
+  if (d->E_heavy > 0 && (!w->w1 || !w->w2 || (d->act == MOE_ACT_SWIGLU && !w->w3))) return MOE_EINVAL;
+  if (d->n_shared > 0 && (!w->s_w1 || !w->s_w2 || (d->act == MOE_ACT_SWIGLU && !w->s_w3))) return MOE_EINVAL;
+  if (d->n_const > 0 && !w->const_vec) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_desc* desc) {
+  Plan p;
+  if (make_plan(desc, &p) != MOE_OK) return 0;
+  return p.total;
+}
+
+moe_status moe_route(const moe_desc* desc, const float* logits, moe_routing* routing, void* ws, size_t ws_bytes,
+                     void* stream) {
+  Plan p;
+  MOE_TRY(make_plan(desc, &p));
+  if (!logits) return MOE_EINVAL;
+  MOE_TRY(check_routing(desc, routing));
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  return do_route(desc, p, logits, (desc->flags & MOE_F_INPUT_PROBS) != 0, routing, ws, (hipStream_t)stream);
+}
+
+moe_status moe_dispatch(const moe_desc* desc, const void* x, const moe_routing* routing, void* x_perm, void* stream) {
+  Plan p;
+  MOE_TRY(make_plan(desc, &p));
+  if (!x || !x_perm || !routing || !routing->row_token || !routing->n_rows) return MOE_EINVAL;
+  return after_launch(launch_gather(desc->dtype, x, routing->row_token, routing->n_rows, x_perm, (int)p.R_max,
+                                    desc->d, (hipStream_t)stream),
+                      desc, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const void* x_perm, const moe_routing* routing,
+                          const moe_weights* weights, float* y_perm, float* y_shared, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Plan p;
+  MOE_TRY(make_plan(desc, &p));
+  if (!x) return MOE_EINVAL;
+  MOE_TRY(check_weights(desc, weights, false));
+  if (desc->E_heavy > 0 && (!routing || !routing->offsets || !routing->row_token || !y_perm)) return MOE_EINVAL;
+  if (desc->n_shared > 0 && !y_shared) return MOE_EINVAL;
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  return do_experts(desc, p, x, x_perm, routing, weights, y_perm, y_shared, ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_desc* desc, const void* x, const moe_routing* routing, const float* y_perm,
+                       const float* y_shared, const void* const_vec, void* cache, const void* residual, void* y,
+                       void* stream) {
+  Plan p;
+  MOE_TRY(make_plan(desc, &p));
+  if (!x || !y || !routing) return MOE_EINVAL;
+  if (desc->mode == MOE_EXPERT_CHOICE) {
+    if (!routing->token_off || !routing->token_list || !routing->row_w) return MOE_EINVAL;
+  } else {
+    if (!routing->topk_idx || !routing->topk_w || !routing->token_rows) return MOE_EINVAL;
+    if (desc->reuse_tau > 0.f && (!routing->reuse || !cache)) return MOE_EINVAL;
+  }
+  if (desc->E_heavy > 0 && !y_perm) return MOE_EINVAL;
+  if (desc->n_shared > 0 && !y_shared) return MOE_EINVAL;
+  if (desc->n_const > 0 && !const_vec) return MOE_EINVAL;
+  return do_combine(desc, p, x, routing, y_perm, y_shared, const_vec, cache, residual, y, (hipStream_t)stream);
+}
+
+moe_status moe_layer_forward(const moe_desc* desc, const void* x, const moe_weights* weights, const float* prev_logits,
+                             float* logits_out, moe_routing* routing, void* cache, const void* residual, void* y,
+                             void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  MOE_TRY(make_plan(desc, &p));
+  if (!x || !y) return MOE_EINVAL;
+  if (desc->flags & MOE_F_INPUT_PROBS) return MOE_EINVAL;
+  MOE_TRY(check_weights(desc, weights, true));
+  if (desc->reuse_tau > 0.f && !cache) return MOE_EINVAL;
+  MOE_TRY(check_ws(p, ws, ws_bytes));
+  moe_routing internal;
+  if (routing) {
+    MOE_TRY(check_routing(desc, routing));
+  } else {
+    internal = internal_routing(p, desc, ws);
+    routing = &internal;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* w = (uint8_t*)ws;
+  float* logits = logits_out ? logits_out : (float*)(w + p.o_logits);
+  MOE_TRY(after_launch(launch_router(desc->dtype, x, weights->w_router, prev_logits, logits, desc->S, desc->d, p.E_r, st),
+                       desc, st));
+  MOE_TRY(do_route(desc, p, logits, false, routing, ws, st));
+  float* y_perm = (float*)(w + p.o_yp);
+  float* y_shared = (float*)(w + p.o_ys);
+  MOE_TRY(do_experts(desc, p, x, nullptr, routing, weights, y_perm, y_shared, ws, st));
+  return do_combine(desc, p, x, routing, y_perm, y_shared, weights->const_vec, cache, residual, y, st);
+}
+
+moe_status moe_profile_begin(void) {
+  if (prof::g_pool.empty()) {
+    prof::g_pool.resize(2 * prof::kPoolPairs);
+    for (auto& e : prof::g_pool)
+      if (hipEventCreate(&e) != hipSuccess) {
+        prof::g_pool.clear();
+        return MOE_EHIP;
+      }
+  }
+  prof::g_recs.clear();
+  prof::g_entries.clear();
+  prof::g_on = true;
+  return MOE_OK;
+}
+
+int moe_profile_end(void) {
+  prof::g_on = false;
+  prof::g_entries.clear();
+  for (const auto& r : prof::g_recs) {
+    if (hipEventSynchronize(r.stop) != hipSuccess) return MOE_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) return MOE_EHIP;
+    bool found = false;
+    for (auto& e : prof::g_entries)
+      if (e.name == r.name) {
+        e.ms += ms;
+        e.launches += 1;
+        found = true;
+        break;
+      }
+    if (!found) prof::g_entries.push_back({r.name, (double)ms, 1});
+  }
+  prof::g_recs.clear();
+  return (int)prof::g_entries.size();
+}
+
+moe_status moe_profile_entry(int i, const char** name, double* total_ms, int32_t* launches) {
+  if (i < 0 || i >= (int)prof::g_entries.size() || !name || !total_ms || !launches) return MOE_EINVAL;
+  *name = prof::g_entries[i].name.c_str();
+  *total_ms = prof::g_entries[i].ms;
+  *launches = prof::g_entries[i].launches;
+  return MOE_OK;
+}
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_EWORKSPACE: return "workspace too small or misaligned";
+    case MOE_EHIP: return "HIP runtime or launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the gfx950 kernels of the MoE layer library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load that bypasses cache retention (for data read exactly once).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Storage element of a bf16 tensor: its 16-bit encoding.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> {
+  static constexpr int kPer16B = 8;   // elements in one 16-byte chunk
+  __device__ static __forceinline__ float to_f(bf16_t v) { return bf16_to_f32(v); }
+  __device__ static __forceinline__ bf16_t from_f(float v) { return f32_to_bf16(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int kPer16B = 4;
+  __device__ static __forceinline__ float to_f(float v) { return v; }
+  __device__ static __forceinline__ float from_f(float v) { return v; }
+};
+
+// Unpack a 16-byte chunk into floats (8 for bf16, 4 for fp32).
+__device__ __forceinline__ void unpack16(const uint4 v, float* out, bf16_t) {
+  out[0] = __uint_as_float(v.x << 16); out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+  out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xFFFF0000u);
+  out[4] = __uint_as_float(v.z << 16); out[5] = __uint_as_float(v.z & 0xFFFF0000u);
+  out[6] = __uint_as_float(v.w << 16); out[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+__device__ __forceinline__ void unpack16(const uint4 v, float* out, float) {
+  out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+}
+__device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
+  uint4 v;
+  v.x = (uint32_t)f32_to_bf16(in[0]) | ((uint32_t)f32_to_bf16(in[1]) << 16);
+  v.y = (uint32_t)f32_to_bf16(in[2]) | ((uint32_t)f32_to_bf16(in[3]) << 16);
+  v.z = (uint32_t)f32_to_bf16(in[4]) | ((uint32_t)f32_to_bf16(in[5]) << 16);
+  v.w = (uint32_t)f32_to_bf16(in[6]) | ((uint32_t)f32_to_bf16(in[7]) << 16);
+  return v;
+}
+__device__ __forceinline__ uint4 pack16(const float* in, float) {
+  return make_uint4(__float_as_uint(in[0]), __float_as_uint(in[1]), __float_as_uint(in[2]), __float_as_uint(in[3]));
+}
+
+// One MFMA step on a 16-byte chunk per lane, for a 16x16 output tile.
+// The lane layout (verified on gfx950): operand P supplies rows i = lane % 16 of the first
+// matrix, operand Q rows j = lane % 16 of the second; lane group g = lane / 16 supplies a slice
+// of the reduction index (the same slice in P and Q, so the slice order does not matter);
+// acc[t] of lane l is D[i = 4*(l/16) + t][j = l % 16], D = sum_k P[i][k] * Q[j][k].
+__device__ __forceinline__ floatx4_t mfma16(const uint4 p, const uint4 q, floatx4_t acc, bf16_t) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p), __builtin_bit_cast(bf16x8_t, q),
+                                                 acc, 0, 0, 0);
+}
+__device__ __forceinline__ floatx4_t mfma16(const uint4 p, const uint4 q, floatx4_t acc, float) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p.x), __uint_as_float(q.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p.y), __uint_as_float(q.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p.z), __uint_as_float(q.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p.w), __uint_as_float(q.w), acc, 0, 0, 0);
+  return acc;
+}
+
+// Activations (MLP hidden layer).
+enum { ACT_GELU = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
+
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ __forceinline__ float gelu_tanh(float z) {
+  return 0.5f * z * (1.0f + tanhf(0.79788456080286536f * (z + 0.044715f * z * z * z)));
+}
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = __lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+}  // namespace moe

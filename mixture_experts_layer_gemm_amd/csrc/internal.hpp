@@ -1,0 +1,143 @@
+// Internal launchers of the MoE layer library (host side). Not part of the C ABI.
+#pragma once
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---------------------------------------------------------------------------------------------
+// Launch-time profiling (off by default). While on, every launch gets a start/stop event pair
+// attached to its dispatch on the launch stream; the pairs are read back by moe_profile_end.
+namespace prof {
+bool enabled();
+// Next free event pair for a launch named `name`; false when the pool is exhausted.
+bool take(const char* name, hipEvent_t* start, hipEvent_t* stop);
+}  // namespace prof
+
+#define MOE_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                                   \
+  do {                                                                                              \
+    hipEvent_t moe_ev0_, moe_ev1_;                                                                  \
+    if (::moe::prof::enabled() && ::moe::prof::take((name), &moe_ev0_, &moe_ev1_))                  \
+      hipExtLaunchKernelGGL((kernel), dim3(grid), dim3(block), (shmem), (stream), moe_ev0_, moe_ev1_, \
+                            0, __VA_ARGS__);                                                        \
+    else                                                                                            \
+      hipLaunchKernelGGL((kernel), dim3(grid), dim3(block), (shmem), (stream), __VA_ARGS__);         \
+  } while (0)
+
+// ---------------------------------------------------------------------------------------------
+// Router: logits[S, E] = x[S, d] . W_r[E, d]^T (+ prev[S, E]).
+hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits,
+                         int S, int d, int E, hipStream_t st);
+
+// ---------------------------------------------------------------------------------------------
+// Routing.
+struct RouteArgs {
+  int S, E_r, E_heavy, k, renorm, input_probs;
+  int n_identity, n_zero, n_const;
+  float tau;
+  int vote_k, m_core;
+  const float* keys;       // logits [S,E_r] or probabilities (input_probs)
+  float* probs;            // [S,E_r] out (nullable)
+  int32_t* topk_idx;       // [S,k]
+  float* topk_w;           // [S,k]
+  uint8_t* reuse;          // [S] (nullable when tau == 0)
+  float* votes;            // DES [E_r]
+  int32_t* core;           // DES [m_core]
+};
+hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st);
+hipError_t launch_route_des(const RouteArgs& a, float* ws_filt /* [S,E_r] */, hipStream_t st);
+
+// Counting sort of (token, slot) pairs to heavy experts (token choice / DES).
+struct PermuteArgs {
+  int S, k, E_r, E_heavy;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const uint8_t* reuse;    // nullable
+  int32_t* counts;         // [E_r]
+  int32_t* offsets;        // [E_r+1]
+  int32_t* row_token;      // [S*k]
+  float* row_w;            // [S*k]
+  int32_t* token_rows;     // [S*k]
+  int32_t* n_rows;         // [1]
+  int32_t* blk_cnt;        // scratch [nblk * E_heavy]
+};
+int permute_num_blocks(int S, int k);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
+
+// Expert choice.
+struct ECArgs {
+  int S, E, C, input_probs;
+  const float* keys;       // logits or probabilities [S,E]
+  float* probs;            // [S,E] out (nullable)
+  float* pT;               // scratch [E,S]
+  uint32_t* tok_mask;      // scratch [S, mask_words]
+  int32_t* tok_rows_tmp;   // scratch [S,E]
+  int32_t* counts;         // [E]
+  int32_t* offsets;        // [E+1]
+  int32_t* row_token;      // [E*C]
+  float* row_w;            // [E*C]
+  int32_t* token_off;      // [S+1]
+  int32_t* token_list;     // [E*C]
+  int32_t* n_rows;         // [1]
+  int32_t* capacity;       // [1] (nullable)
+};
+hipError_t launch_route_ec(const ECArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------------------------
+// Dispatch / combine.
+hipError_t launch_gather(int dtype, const void* x, const int32_t* row_token, const int32_t* n_rows, void* x_perm,
+                         int R_max, int d, hipStream_t st);
+
+struct CombineArgs {
+  int dtype, mode, S, d, k, E_heavy, n_identity, n_zero, n_const;
+  const void* x;
+  const int32_t* topk_idx;
+  const float* topk_w;
+  const int32_t* token_rows;
+  const int32_t* token_off;
+  const int32_t* token_list;
+  const float* row_w;
+  const uint8_t* reuse;     // nullable
+  const float* y_perm;
+  const float* y_shared;    // nullable
+  const void* const_vec;    // nullable
+  void* cache;              // nullable
+  const void* residual;     // nullable
+  void* y;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t st);
+
+// ---------------------------------------------------------------------------------------------
+// Grouped GEMMs.
+//
+// One problem: groups g = 0..G-1 of rows. Group g's rows are [offsets[g], offsets[g+1]) of the
+// output (offsets != null; data-dependent, read on the device), or rows [0, M_uni) (offsets == null).
+//   A row of output row r: a_rows ? a_rows[r] : r      (row of A, length K, stride lda)
+//   B: weights of group g at B + g*b_gstride, row n at + n*ldb; K split into segments of k_seg
+//      elements placed k_seg_stride apart (a K-concatenation of several experts' weights).
+//   C: row r, column g*c_gcol + n, stride ldc.
+struct GemmProblem {
+  const void* A; const int32_t* a_rows; int64_t lda;
+  const void* B; const void* B3; int64_t ldb; int64_t b_gstride;
+  int64_t k_seg, k_seg_stride;
+  void* C; int64_t ldc; int64_t c_gcol;
+  const int32_t* offsets; int32_t G, M_uni;
+  int32_t N, K;            // N = output columns per group
+};
+enum { GEMM_UP = 0, GEMM_DOWN = 1 };
+// kind GEMM_UP: C (dtype) = act(A.B^T) (SwiGLU: silu(A.B3^T) * (A.B^T)); GEMM_DOWN: C (fp32) = A.B^T.
+// `rows_ub[i]` bounds the total rows of problem i (for the grid).
+hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* probs, const int64_t* rows_ub,
+                               int nprob, hipStream_t st);
+bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K);
+
+// Weight-streaming grouped GEMM for few rows per expert; grid.y = max_active bounds the number
+// of experts with rows (offsets-based problems only).
+hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, hipStream_t st);
+bool stream_gemm_supported(int dtype, int kind, int act, int N, int K);
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
+
+}  // namespace moe

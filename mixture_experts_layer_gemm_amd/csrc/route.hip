@@ -1,0 +1,483 @@
+// Router GEMM, softmax + token-choice top-k, DES-Vote core set, and the counting-sort dispatch.
+//
+// Router and affinity: "EC-DiT: Scaling Diffusion Transformers with Adaptive Expert-Choice
+// Routing", 三 技术架构 / 核心公式 (scores x' W_r, A = softmax over experts; token choice takes each
+// token's top-k experts). Gate residual: "MMOE: Modernizing Diffusion Transformers with Efficient
+// Expert Design", 方法论 (the router adds the previous MoE layer's logits). DES-Vote: "Dynamic
+// Expert Sharing: Decoupling Memory from Parallelism in Mixture-of-Experts Diffusion LLMs", 2.4
+// (filter to top-K, vote with routing weights, elect M_core) and 4.3 (re-activate top-k inside the
+// core). Low-score reuse mask: "DICE: Staleness-Centric Optimizations for Parallel Diffusion MoE
+// Inference", 关键设计 / 条件通信.
+//
+// Selection order everywhere: key descending, expert index ascending on ties. Keys are the fp32
+// logits (or given probabilities), compared exactly.
+#include <float.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace moe {
+
+// =============================================================================================
+// Router GEMM. One wave computes 16 tokens x all experts with 16x16 MFMA tiles: operand P = W_r
+// rows (16 experts), operand Q = x rows (16 tokens), so each lane ends with 4 consecutive experts
+// of one token. x is read once from HBM; W_r (a few KB to a few hundred KB) stays in cache.
+template <typename T>
+__global__ __launch_bounds__(64) void k_router(const T* __restrict__ x, const T* __restrict__ w,
+                                               const float* __restrict__ prev, float* __restrict__ logits,
+                                               int S, int d, int E) {
+  constexpr int EPC = Elem<T>::kPer16B;
+  const int lane = threadIdx.x;
+  const int r = lane & 15, g = lane >> 4;
+  const int s0 = blockIdx.x * 16;
+  const int s = min(s0 + r, S - 1);
+  const T* xrow = x + (size_t)s * d + g * EPC;
+  const int e_tiles = (E + 15) >> 4;
+  for (int et0 = 0; et0 < e_tiles; et0 += 4) {
+    floatx4_t acc[4];
+    const T* wrow[4];
+    bool wok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      const int e = (et0 + q) * 16 + r;
+      wok[q] = e < E;
+      wrow[q] = w + (size_t)min(e, E - 1) * d + g * EPC;
+    }
+#pragma unroll 4
+    for (int kk = 0; kk < d; kk += 4 * EPC) {
+      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + kk);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (et0 + q < e_tiles) {
+          uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
+          if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
+          acc[q] = mfma16(wv, xv, acc[q], T());
+        }
+      }
+    }
+    const int st = s0 + r;
+    if (st < S) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int e = (et0 + q) * 16 + 4 * g + t;
+          if (et0 + q < e_tiles && e < E) {
+            float v = acc[q][t];
+            if (prev) v += prev[(size_t)st * E + e];
+            logits[(size_t)st * E + e] = v;
+          }
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits, int S,
+                         int d, int E, hipStream_t st) {
+  const int blocks = (S + 15) / 16;
+  if (dtype == 0) {
+    auto kfn = k_router<bf16_t>;
+    MOE_LAUNCH("router", kfn, blocks, 64, 0, st, (const bf16_t*)x, (const bf16_t*)w_router, prev, logits, S, d, E);
+  } else {
+    auto kfn = k_router<float>;
+    MOE_LAUNCH("router", kfn, blocks, 64, 0, st, (const float*)x, (const float*)w_router, prev, logits, S, d, E);
+  }
+  return hipGetLastError();
+}
+
+// =============================================================================================
+// Group primitives: a token's experts are spread over LPT lanes (LPT a power of two <= 64), each
+// lane holding V = ceil(E/LPT) of them (expert e lives in lane e % LPT, slot e / LPT).
+template <int LPT>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+template <int LPT>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Arg-best over the group under (key desc, index asc).
+template <int LPT>
+__device__ __forceinline__ void group_argbest(float& key, int& idx) {
+#pragma unroll
+  for (int o = LPT / 2; o > 0; o >>= 1) {
+    const float ok = __shfl_xor(key, o, 64);
+    const int oi = __shfl_xor(idx, o, 64);
+    if (ok > key || (ok == key && oi < idx)) { key = ok; idx = oi; }
+  }
+}
+
+constexpr int kMaxV = 4;   // E_r <= 256
+
+// Per-token probabilities from logits (softmax with the row max subtracted) or as given.
+template <int LPT, int V>
+__device__ __forceinline__ void token_probs(const float* keys_row, bool live, int E, int sub, int input_probs,
+                                            float (&key)[V], float (&p)[V]) {
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int e = sub + v * LPT;
+    key[v] = (live && e < E) ? keys_row[e] : -FLT_MAX;
+  }
+  if (input_probs) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) p[v] = (sub + v * LPT < E) ? key[v] : 0.f;
+    return;
+  }
+  float m = -FLT_MAX;
+#pragma unroll
+  for (int v = 0; v < V; ++v) m = fmaxf(m, key[v]);
+  m = group_max<LPT>(m);
+  float z[V], zs = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    z[v] = (sub + v * LPT < E) ? expf(key[v] - m) : 0.f;
+    zs += z[v];
+  }
+  zs = group_sum<LPT>(zs);
+  const float inv = 1.0f / zs;
+#pragma unroll
+  for (int v = 0; v < V; ++v) p[v] = z[v] * inv;
+}
+
+constexpr int kMaxK = 16;
+
+// Top-k of the token's keys among experts allowed by `allow` (bit v of the lane's mask).
+// Returns the lane's chosen-set bits; when sel_e is given (k <= kMaxK) also writes the k chosen
+// experts and their probabilities in key order.
+template <int LPT, int V>
+__device__ __forceinline__ unsigned token_topk(const float (&key)[V], const float (&p)[V], unsigned allow, int E,
+                                               int sub, int lane, int k, int* sel_e, float* sel_p) {
+  unsigned taken = 0;
+  for (int j = 0; j < k; ++j) {
+    float bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sub + v * LPT;
+      const bool ok = e < E && ((allow >> v) & 1u) && !((taken >> v) & 1u);
+      if (ok && (key[v] > bk || (key[v] == bk && e < bi))) { bk = key[v]; bi = e; }
+    }
+    group_argbest<LPT>(bk, bi);
+    // owner lane of expert bi supplies its probability
+    float mine = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (sub + v * LPT == bi) { mine = p[v]; taken |= 1u << v; }
+    const int owner = (lane & ~(LPT - 1)) + (bi & (LPT - 1));
+    const float pw = __shfl(mine, owner, 64);
+    if (sel_e) {
+      sel_p[j] = pw;
+      sel_e[j] = bi;
+    }
+  }
+  return taken;
+}
+
+template <int LPT, int V>
+__global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & (LPT - 1);
+  const int s = blockIdx.x * (256 / LPT) + threadIdx.x / LPT;
+  const bool live = s < a.S;
+  const int E = a.E_r;
+  float key[V], p[V];
+  token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
+  if (live && a.probs) {
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (sub + v * LPT < E) a.probs[(size_t)s * E + sub + v * LPT] = p[v];
+  }
+  float pm = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
+  pm = group_max<LPT>(pm);
+  int sel_e[kMaxK];
+  float sel_p[kMaxK];
+  token_topk<LPT, V>(key, p, ~0u, E, sub, lane, a.k, sel_e, sel_p);
+  if (live && sub == 0) {
+    float denom = 1.f;
+    if (a.renorm) {
+      float t = 0.f;
+      for (int j = 0; j < a.k; ++j) t += sel_p[j];
+      denom = t;
+    }
+    for (int j = 0; j < a.k; ++j) {
+      a.topk_idx[(size_t)s * a.k + j] = sel_e[j];
+      a.topk_w[(size_t)s * a.k + j] = a.renorm ? sel_p[j] / denom : sel_p[j];
+    }
+    if (a.reuse) a.reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
+  }
+}
+
+template <int LPT, int V>
+static void route_topk_t(const RouteArgs& a, hipStream_t st) {
+  auto kfn = k_route_topk<LPT, V>;
+  MOE_LAUNCH("route_topk", kfn, (a.S + 256 / LPT - 1) / (256 / LPT), 256, 0, st, a);
+}
+
+hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st) {
+  const int E = a.E_r;
+  if (E <= 8) route_topk_t<8, 1>(a, st);
+  else if (E <= 16) route_topk_t<16, 1>(a, st);
+  else if (E <= 32) route_topk_t<32, 1>(a, st);
+  else if (E <= 64) route_topk_t<64, 1>(a, st);
+  else if (E <= 128) route_topk_t<64, 2>(a, st);
+  else route_topk_t<64, 4>(a, st);
+  return hipGetLastError();
+}
+
+// =============================================================================================
+// DES-Vote, one workgroup for the whole block of N tokens (N = a.S).
+//  1. per token: probabilities, top-K filter T_n; filt[n][e] = p_{n,e} for e in T_n, else 0;
+//  2. per expert: v_e = sum over n ascending of filt[n][e] (fp32, sequential: adding the zeros
+//     of unfiltered entries leaves the sum unchanged);
+//  3. core = the m_core experts first under (v desc, e asc), listed ascending;
+//  4. per token: top-min(k, m_core) by key among core experts; weights p or renormalised p.
+template <int LPT, int V>
+__global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restrict__ filt) {
+  __shared__ float s_votes[256];
+  __shared__ int s_incore[256];
+  const int lane = threadIdx.x & 63;
+  const int sub = lane & (LPT - 1);
+  const int tpb = 256 / LPT;
+  const int E = a.E_r;
+  // 1. filter
+  for (int base = 0; base < a.S; base += tpb) {
+    const int s = base + threadIdx.x / LPT;
+    const bool live = s < a.S;
+    float key[V], p[V];
+    token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
+    const unsigned taken = token_topk<LPT, V>(key, p, ~0u, E, sub, lane, a.vote_k, nullptr, nullptr);
+    float pm = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
+    pm = group_max<LPT>(pm);
+    if (live) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = sub + v * LPT;
+        if (e < E) {
+          filt[(size_t)s * E + e] = ((taken >> v) & 1u) ? p[v] : 0.f;
+          if (a.probs) a.probs[(size_t)s * E + e] = p[v];
+        }
+      }
+      if (sub == 0 && a.reuse) a.reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  // 2. votes
+  for (int e = threadIdx.x; e < E; e += 256) {
+    float v = 0.f;
+    for (int n = 0; n < a.S; ++n) v += filt[(size_t)n * E + e];
+    s_votes[e] = v;
+    a.votes[e] = v;
+  }
+  __syncthreads();
+  // 3. elect
+  for (int e = threadIdx.x; e < E; e += 256) {
+    const float ve = s_votes[e];
+    int rank = 0;
+    for (int q = 0; q < E; ++q) {
+      const float vq = s_votes[q];
+      rank += (vq > ve || (vq == ve && q < e)) ? 1 : 0;
+    }
+    s_incore[e] = rank < a.m_core ? 1 : 0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    if (s_incore[e]) {
+      int pos = 0;
+      for (int q = 0; q < e; ++q) pos += s_incore[q];
+      a.core[pos] = e;
+    }
+  }
+  // 4. re-route inside the core
+  const int kk = min(a.k, a.m_core);
+  for (int base = 0; base < a.S; base += tpb) {
+    const int s = base + threadIdx.x / LPT;
+    const bool live = s < a.S;
+    float key[V], p[V];
+    token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
+    unsigned allow = 0;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = sub + v * LPT;
+      if (e < E && s_incore[e]) allow |= 1u << v;
+    }
+    int sel_e[kMaxK];
+    float sel_p[kMaxK];
+    token_topk<LPT, V>(key, p, allow, E, sub, lane, kk, sel_e, sel_p);
+    if (live && sub == 0) {
+      float denom = 1.f;
+      if (a.renorm) {
+        float t = 0.f;
+        for (int j = 0; j < kk; ++j) t += sel_p[j];
+        denom = t;
+      }
+      for (int j = 0; j < kk; ++j) {
+        a.topk_idx[(size_t)s * kk + j] = sel_e[j];
+        a.topk_w[(size_t)s * kk + j] = a.renorm ? sel_p[j] / denom : sel_p[j];
+      }
+    }
+  }
+}
+
+template <int LPT, int V>
+static void route_des_t(const RouteArgs& a, float* ws_filt, hipStream_t st) {
+  auto kfn = k_route_des<LPT, V>;
+  MOE_LAUNCH("route_des", kfn, 1, 256, 0, st, a, ws_filt);
+}
+
+hipError_t launch_route_des(const RouteArgs& a, float* ws_filt, hipStream_t st) {
+  const int E = a.E_r;
+  if (E <= 8) route_des_t<8, 1>(a, ws_filt, st);
+  else if (E <= 16) route_des_t<16, 1>(a, ws_filt, st);
+  else if (E <= 32) route_des_t<32, 1>(a, ws_filt, st);
+  else if (E <= 64) route_des_t<64, 1>(a, ws_filt, st);
+  else if (E <= 128) route_des_t<64, 2>(a, ws_filt, st);
+  else route_des_t<64, 4>(a, ws_filt, st);
+  return hipGetLastError();
+}
+
+// =============================================================================================
+// Counting sort of the (token, slot) pairs onto heavy experts. Pair p = s*k + j. A pair is
+// dispatched when its expert is heavy and its token does not reuse its cache. Rows are grouped by
+// expert ascending; inside an expert, by p ascending (token, then slot). Three passes, no atomics
+// on the output order: per-chunk histograms, a scan, and a ranked scatter.
+constexpr int kPermThreads = 256;
+constexpr int kPermRounds = 4;
+constexpr int kPermChunk = kPermThreads * kPermRounds;
+constexpr int kPermMaxE = 1024;
+
+int permute_num_blocks(int S, int k) { return (int)(((int64_t)S * k + kPermChunk - 1) / kPermChunk); }
+
+__device__ __forceinline__ bool pair_live(const PermuteArgs& a, int64_t p, int& e) {
+  if (p >= (int64_t)a.S * a.k) { e = -1; return false; }
+  e = a.topk_idx[p];
+  const int s = (int)(p / a.k);
+  return e >= 0 && e < a.E_heavy && !(a.reuse && a.reuse[s]);
+}
+
+__global__ __launch_bounds__(kPermThreads) void k_perm_count(PermuteArgs a) {
+  __shared__ int cnt[kPermMaxE];
+  for (int i = threadIdx.x; i < a.E_heavy; i += kPermThreads) cnt[i] = 0;
+  __syncthreads();
+  for (int r = 0; r < kPermRounds; ++r) {
+    const int64_t p = (int64_t)blockIdx.x * kPermChunk + r * kPermThreads + threadIdx.x;
+    int e;
+    if (pair_live(a, p, e)) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.E_heavy; i += kPermThreads) a.blk_cnt[(size_t)blockIdx.x * a.E_heavy + i] = cnt[i];
+}
+
+// One workgroup: per-expert exclusive bases over chunks (in place), counts, offsets.
+__global__ __launch_bounds__(kPermThreads) void k_perm_scan(PermuteArgs a, int nblk) {
+  __shared__ int tot[kPermMaxE];
+  for (int e = threadIdx.x; e < a.E_heavy; e += kPermThreads) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int c = a.blk_cnt[(size_t)b * a.E_heavy + e];
+      a.blk_cnt[(size_t)b * a.E_heavy + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int e = 0; e < a.E_r; ++e) {
+      const int c = e < a.E_heavy ? tot[e] : 0;
+      a.offsets[e] = run;
+      a.counts[e] = c;
+      run += c;
+    }
+    a.offsets[a.E_r] = run;
+    *a.n_rows = run;
+  }
+}
+
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a, int nbits) {
+  __shared__ int wcnt[kPermThreads / 64][kPermMaxE];
+  __shared__ int run[kPermMaxE];
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < a.E_heavy; i += kPermThreads) {
+    run[i] = 0;
+    for (int w = 0; w < kPermThreads / 64; ++w) wcnt[w][i] = 0;
+  }
+  __syncthreads();
+  const int* bbase = a.blk_cnt + (size_t)blockIdx.x * a.E_heavy;
+  for (int r = 0; r < kPermRounds; ++r) {
+    const int64_t p = (int64_t)blockIdx.x * kPermChunk + r * kPermThreads + threadIdx.x;
+    int e;
+    const bool ok = pair_live(a, p, e);
+    const int key = ok ? e : a.E_heavy;       // one extra class for pairs not dispatched
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t lower = peers & lanemask_lt();
+    const int rank = __popcll(lower);
+    if (ok && lower == 0) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int base = run[e];
+      for (int w = 0; w < wave; ++w) base += wcnt[w][e];
+      const int row = a.offsets[e] + bbase[e] + base + rank;
+      a.row_token[row] = (int)(p / a.k);
+      a.row_w[row] = a.topk_w[p];
+      a.token_rows[p] = row;
+    } else if (p < (int64_t)a.S * a.k) {
+      a.token_rows[p] = -1;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.E_heavy; i += kPermThreads) {
+      int add = 0;
+      for (int w = 0; w < kPermThreads / 64; ++w) { add += wcnt[w][i]; wcnt[w][i] = 0; }
+      run[i] += add;
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
+  const int nblk = permute_num_blocks(a.S, a.k);
+  int nbits = 1;
+  while ((1 << nbits) <= a.E_heavy) ++nbits;   // classes 0..E_heavy
+  if (nblk > 0) {
+    auto kfn = k_perm_count;
+    MOE_LAUNCH("perm_count", kfn, nblk, kPermThreads, 0, st, a);
+  }
+  {
+    auto kfn = k_perm_scan;
+    MOE_LAUNCH("perm_scan", kfn, 1, kPermThreads, 0, st, a, nblk);
+  }
+  if (nblk > 0) {
+    auto kfn = k_perm_scatter;
+    MOE_LAUNCH("perm_scatter", kfn, nblk, kPermThreads, 0, st, a, nbits);
+  }
+  return hipGetLastError();
+}
+
+// =============================================================================================
+__global__ void k_fill_u32(uint32_t* __restrict__ p, uint32_t v, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  auto kfn = k_fill_u32;
+  MOE_LAUNCH("fill_u32", kfn, blocks, 256, 0, st, p, v, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU (no GPU calls): it loads, exports every entry point include/moe.h
+declares, and rejects bad arguments with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_layer_gemm_amd as moe
+from synth import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # a non-null address; never dereferenced (every case fails validation first)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(moe.lib_path()):
+        from mixture_experts_layer_gemm_amd.build import build
+        build()
+    moe.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    return set(re.findall(r"^\s*(?:const\s+char\s*\*\s*|size_t\s+|moe_status\s+|int\s+)(moe_\w+)\s*\(", src, flags=re.M))
+
+
+def test_exports_every_declared_entry_point():
+    names = _declared()
+    assert names == set(moe.EXPORTS)
+    L = ctypes.CDLL(moe.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror():
+    assert moe.moe_strerror(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert moe.moe_strerror(s) != "unknown status"
+    assert moe.moe_strerror(-99) == "unknown status"
+
+
+def test_workspace_sizes_for_workloads():
+    for spec in WORKLOADS.values():
+        n = moe.moe_workspace_bytes(moe.desc_from_spec(spec))
+        assert n >= 256 and n % 256 == 0
+
+
+def _desc(**kw):
+    d = moe.desc_from_spec(WORKLOADS["dit_moe_xl"])
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+INVALID = [
+    dict(k=0), dict(k=9), dict(S=0), dict(d=0), dict(E_heavy=-1), dict(dtype=7), dict(act=5), dict(mode=3),
+    dict(d_ff=0), dict(reuse_tau=-0.5), dict(reuse_tau=float("nan")), dict(flags=0x1000),
+    dict(flags=moe.MOE_F_FORCE_TILED | moe.MOE_F_FORCE_STREAM),
+    dict(mode=moe.MOE_DES_VOTE, m_core=0, vote_k=8), dict(mode=moe.MOE_DES_VOTE, m_core=9, vote_k=2),
+    dict(mode=moe.MOE_DES_VOTE, m_core=4, vote_k=0),
+    dict(mode=moe.MOE_EXPERT_CHOICE, capacity_factor=0.0),
+    dict(mode=moe.MOE_EXPERT_CHOICE, capacity_factor=0.0009),            # C rounds to 0
+    dict(E_heavy=0, n_identity=0, n_zero=0, n_const=0),
+]
+
+UNSUPPORTED = [
+    dict(d=1160),                                   # router needs d % 32 (bf16)
+    dict(E_heavy=300),                              # more than 256 routed experts
+    dict(k=8, E_heavy=40),                          # fine ...
+    dict(k=17, E_heavy=40),                         # ... but k > 16 is not implemented
+    dict(mode=moe.MOE_EXPERT_CHOICE, n_zero=1),     # zero-computation experts under expert choice
+    dict(d_ff=4600),                                # GEMM tiles need d_ff % 64
+]
+
+
+@pytest.mark.parametrize("kw", INVALID)
+def test_invalid_descriptors(kw):
+    d = _desc(**kw)
+    assert moe.moe_workspace_bytes(d) == 0
+    st = moe.moe_layer_forward(d, FAKE, moe.MoeWeights(*([FAKE] * 8)), None, None, None, FAKE, None, FAKE, FAKE,
+                               1 << 40, stream=0, raise_on_error=False)
+    assert st == moe.MOE_EINVAL
+
+
+@pytest.mark.parametrize("kw", UNSUPPORTED)
+def test_unsupported_descriptors(kw):
+    d = _desc(**kw)
+    if kw == dict(k=8, E_heavy=40):
+        assert moe.moe_workspace_bytes(d) > 0
+        return
+    assert moe.moe_workspace_bytes(d) == 0
+    st = moe.moe_layer_forward(d, FAKE, moe.MoeWeights(*([FAKE] * 8)), None, None, None, FAKE, None, FAKE, FAKE,
+                               1 << 40, stream=0, raise_on_error=False)
+    assert st == moe.MOE_EUNSUPPORTED
+
+
+def test_null_pointers_and_workspace():
+    d = _desc()
+    w = moe.MoeWeights(*([FAKE] * 8))
+    call = lambda **kw: moe.moe_layer_forward(  # noqa: E731
+        d, kw.get("x", FAKE), kw.get("w", w), None, None, None, FAKE, None, kw.get("y", FAKE), kw.get("ws", FAKE),
+        kw.get("nb", 1 << 40), stream=0, raise_on_error=False)
+    assert call(x=None) == moe.MOE_EINVAL
+    assert call(y=None) == moe.MOE_EINVAL
+    assert call(w=moe.MoeWeights(None, *([FAKE] * 7))) == moe.MOE_EINVAL          # no router weight
+    assert call(w=moe.MoeWeights(FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE)) == moe.MOE_EINVAL  # SwiGLU w3
+    assert call(ws=None) == moe.MOE_EWORKSPACE
+    assert call(nb=1024) == moe.MOE_EWORKSPACE
+    assert call(ws=FAKE + 8) == moe.MOE_EWORKSPACE                                 # misaligned
+    # the reuse variant needs a cache
+    d2 = moe.desc_from_spec(WORKLOADS["dit_moe_xl_reuse"])
+    st = moe.moe_layer_forward(d2, FAKE, w, None, None, None, None, None, FAKE, FAKE, 1 << 40, stream=0,
+                               raise_on_error=False)
+    assert st == moe.MOE_EINVAL
+    # probabilities are an input of moe_route only
+    d3 = _desc(flags=moe.MOE_F_INPUT_PROBS)
+    st = moe.moe_layer_forward(d3, FAKE, w, None, None, None, FAKE, None, FAKE, FAKE, 1 << 40, stream=0,
+                               raise_on_error=False)
+    assert st == moe.MOE_EINVAL
+
+
+def test_route_and_combine_argument_checks():
+    d = _desc()
+    r = moe.MoeRouting()
+    assert moe.moe_route(d, FAKE, r, FAKE, 1 << 40, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert moe.moe_route(d, None, r, FAKE, 1 << 40, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    full = moe.MoeRouting(*([FAKE] * 15))
+    assert moe.moe_route(d, FAKE, full, FAKE, 16, stream=0, raise_on_error=False) == moe.MOE_EWORKSPACE
+    assert moe.moe_dispatch(d, None, full, FAKE, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert moe.moe_combine(d, FAKE, full, None, FAKE, None, None, None, FAKE, stream=0,
+                           raise_on_error=False) == moe.MOE_EINVAL       # heavy experts need y_perm
+    assert moe.moe_combine(d, FAKE, full, FAKE, None, None, None, None, FAKE, stream=0,
+                           raise_on_error=False) == moe.MOE_EINVAL       # shared experts need y_shared
+    assert moe.moe_expert_ffn(d, FAKE, None, full, moe.MoeWeights(*([FAKE] * 8)), FAKE, FAKE, FAKE, 16, stream=0,
+                              raise_on_error=False) == moe.MOE_EWORKSPACE
+
+
+def test_binding_raises_with_status():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_route(_desc(k=0), FAKE, moe.MoeRouting(), FAKE, 1, stream=0)
+    assert ei.value.status == moe.MOE_EINVAL
