@@ -23,7 +23,7 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     # keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32)
-    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-inline-asm",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

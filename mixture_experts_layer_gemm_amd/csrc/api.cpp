@@ -112,11 +112,11 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
     return MOE_EUNSUPPORTED;
   if (d->d % 8 != 0) return MOE_EUNSUPPORTED;
   if (d->d % (d->dtype == MOE_BF16 ? 32 : 16) != 0) return MOE_EUNSUPPORTED;   // router MFMA steps
-  // kernels index rows of x, H and y_perm with 32-bit element offsets
+  // kernels address rows of x, H, y_perm and one expert's weights with 32-bit byte offsets
   const int64_t lim = ((int64_t)1 << 31) - 1;
-  const int64_t ff = std::max(d->d_ff, 0);
-  if ((int64_t)d->S * E_r > lim || p->R_max > lim || (int64_t)d->S * d->d > lim || p->R_max * ff > lim ||
-      p->R_max * d->d > lim || (int64_t)d->S * d->n_shared * ff > lim || ff * d->d > lim)
+  const int64_t ff = std::max(d->d_ff, 0), es = d->dtype == MOE_BF16 ? 2 : 4;
+  if ((int64_t)d->S * E_r > lim || p->R_max > lim || (int64_t)d->S * d->d * es > lim || p->R_max * ff * es > lim ||
+      p->R_max * d->d * 4 > lim || (int64_t)d->S * d->n_shared * ff * es > lim || ff * d->d * es > lim)
     return MOE_EUNSUPPORTED;
   const int act = d->act;
   if (d->E_heavy > 0) {

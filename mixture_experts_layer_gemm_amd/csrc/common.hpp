@@ -83,11 +83,31 @@ __device__ __forceinline__ floatx4_t mfma16(const uint4 p, const uint4 q, floatx
 // Activations (MLP hidden layer).
 enum { ACT_GELU = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
 
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
-__device__ __forceinline__ float gelu_tanh(float z) {
-  return 0.5f * z * (1.0f + tanhf(0.79788456080286536f * (z + 0.044715f * z * z * z)));
+// e^x through the hardware base-2 exponential (about 1 ulp).
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// erf by the rational approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (|error| <= 1.5e-7): erf(x) = 1 - (a1 t + ... + a5 t^5) e^{-x^2}, t = 1/(1 + p x),
+// x >= 0, odd extension for x < 0. Far below the bf16 rounding of the stored activation.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = fast_rcp(fmaf(0.3275911f, ax, 1.0f));
+  float y = fmaf(1.061405429f, t, -1.453152027f);
+  y = fmaf(y, t, 1.421413741f);
+  y = fmaf(y, t, -0.284496736f);
+  y = fmaf(y, t, 0.254829592f);
+  y = y * t;
+  const float e = 1.0f - y * fast_exp(-ax * ax);
+  return copysignf(e, x);
 }
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f)); }
+// tanh form: 0.5 z (1 + tanh(u)) = z - z / (1 + e^{2u}), u = sqrt(2/pi) (z + 0.044715 z^3)
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float u = 0.79788456080286536f * fmaf(0.044715f * z, z * z, z);
+  return z - z * fast_rcp(1.0f + fast_exp(2.0f * u));
+}
+__device__ __forceinline__ float silu(float z) { return z * fast_rcp(1.0f + fast_exp(-z)); }
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int l = __lane_id();

@@ -8,7 +8,8 @@
 // experts are extra problems in the same launch (all S rows; their down projections are one GEMM
 // over the K-concatenation of their hidden activations).
 //
-// Design (one workgroup = 4 waves = one 256 x BN output tile, BN in {128, 256}):
+// Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 256}; each wave
+// owns 128 rows x BN/2 weight rows, which keeps LDS reads at 2/3 of a 128 x 64 split):
 //   * K advances 128 bytes per stage (64 bf16 / 32 fp32); A and B stages are double-buffered in
 //     LDS (2 x (32 KB + BN*128 B)) and filled by direct global->LDS loads (no staging registers),
 //     one barrier per stage; stage k+1's loads are in flight while stage k feeds the MFMAs.
@@ -21,14 +22,19 @@
 //     contiguous range, swept as 8 m-tiles x all n-tiles, which keeps an expert's weight panels and
 //     token panels in one XCD's L2.
 //   * The expert of an m-tile comes from a wave-wide scan of ceil(count_e / 256) over experts.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
 constexpr int kBM = 256;
-constexpr int kRowB = 128;          // bytes of one tile row per stage
-constexpr int kThreads = 256;
+constexpr int kRowB = 64;           // bytes of one tile row per stage (one MFMA K-step)
+constexpr int kStages = 4;          // LDS ring: three stages in flight while one is consumed
+constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
+constexpr int kWaves = 4;           // 2 x 2 wave grid, one wave per SIMD
+constexpr int kThreads = 64 * kWaves;
 constexpr int kGM = 8;              // m-tiles per sweep group
 
 struct GemmLaunch {
@@ -40,17 +46,41 @@ struct GemmLaunch {
   int32_t total_tiles;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// 16-byte chunk c (0..3) of tile row r sits at slot c ^ ((r >> 2) & 3): the 16-byte fragment reads
+// of 16 consecutive rows then cover all 64 banks once.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave writes
-// LDS[dst + 16*l]. dst must be the same for the whole wave.
-__device__ __forceinline__ void gload_lds16(const void* src, uint8_t* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)dst, 16, 0, 0);
+// 16 bytes per lane from global memory (wave-uniform base + per-lane byte offset) straight into
+// LDS: lane l of the wave writes LDS[lds_addr + 16*l]; lds_addr is the same for the whole wave (M0). Completion is tracked by
+// the wave's vmcnt, which the K loop waits on explicitly (wait_vmem) before a stage is read. The
+// instruction is issued from inline assembly so the compiler does not add its own wait for every
+// LDS DMA in flight before each LDS read (it cannot tell the ring's stages apart). Nothing else
+// in these kernels uses M0.
+__device__ __forceinline__ void gload_lds16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base),
+               "s"(lds_addr)
+               : "memory", "m0");
 }
-// Wait until this wave's outstanding global loads (including loads into LDS) have completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(const lds_u8_t*)p; }
+// Wait until at most N of this wave's global loads (including loads into LDS) are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier for the LDS ring. Every wave has already waited for its own loads of the
+// stage it needs (wait_vmem) and for its LDS reads (lgkmcnt 0), so no memory fence is needed (a
+// fence would also wait for the stages still in flight). The empty asm statements keep the
+// compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 // Map m-tile `mt` of problem P to (group, first row, rows). Returns false for a tile past the end.
 __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& g, int& row0, int& rows) {
@@ -109,6 +139,17 @@ __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& 
   return g >= 0;
 }
 
+// Scheduling pattern for the K step: NF times (one LDS read, then its share of the NM MFMAs).
+template <int NM, int NF, int Q = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (Q < NF) {
+    constexpr int cnt = (Q + 1 < NF ? ((Q + 1) * NM) / NF : NM) - (Q * NM) / NF;
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // DS read
+    if constexpr (cnt > 0) __builtin_amdgcn_sched_group_barrier(0x008, cnt, 0);   // MFMA
+    sched_interleave<NM, NF, Q + 1>();
+  }
+}
+
 template <typename T, int KIND, int ACT, int BN>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int EPC = Elem<T>::kPer16B;        // elements per 16-byte chunk
@@ -116,19 +157,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
   constexpr int NI = BN / 32;                  // 16-row n-subtiles per wave (wave covers BN/2 B rows)
   constexpr int MJ = 8;                        // 16-row m-subtiles per wave (wave covers 128 rows)
+  constexpr int NF = MJ + NI;                  // fragments per K step
   constexpr int A_BYTES = kBM * kRowB;
   constexpr int B_BYTES = BN * kRowB;
   constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LD = kBM / 32;               // wave load instructions per stage (8 rows x 128 B each)
-  constexpr int B_LD = BN / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int A_LD = kBM / (kRowsPerLoad * kWaves);   // wave load instructions per stage
+  constexpr int B_LD = BN / (kRowsPerLoad * kWaves);
+  constexpr int LPS = A_LD + B_LD;                       // loads per wave per stage
+  // One array per ring stage: with the K loop unrolled by kStages every LDS access names its stage
+  // at compile time.
+  static_assert(kStages == 4, "the ring below is written for four stages");
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem2[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem3[STAGE];
 
   // ---- tile decode (XCD-contiguous renumbering)
   const int nb = gridDim.x;
   const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
   if (L >= args.total_tiles) return;
   const bool second = args.nprob > 1 && L >= args.tile_begin1;
-  const GemmProblem& P = second ? args.p1 : args.p0;
+  const GemmProblem P = second ? args.p1 : args.p0;   // a copy: kept in scalar registers
   const int Lq = second ? L - args.tile_begin1 : L;
   const int tn = second ? args.tiles_n1 : args.tiles_n0;
   const int mt_ub = second ? args.mt_ub1 : args.mt_ub0;
@@ -141,45 +190,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   if (!locate_mtile(P, mt, g, row0, rows)) return;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-lane source offsets. Load instruction i of wave w fills tile rows i*32 + 8w .. +8;
-  // lane l writes row r = i*32 + 8w + l/8 at slot l%8, i.e. chunk (l%8) ^ ((r >> 1) & 7).
+  // ---- per-lane source offsets. Load instruction i of wave w fills tile rows
+  // i*16*kWaves + 16w .. +16; lane l writes row r = i*16*kWaves + 16w + l/4 at slot l%4, i.e. the
+  // chunk (l%4) ^ ((r >> 2) & 3) of that row.
   const T* __restrict__ Ab = (const T*)P.A;
   const T* __restrict__ Bb = (const T*)P.B + (size_t)g * P.b_gstride;
   const T* __restrict__ B3b = SWIGLU ? (const T*)P.B3 + (size_t)g * P.b_gstride : nullptr;
+  // byte offsets of this lane's 16 bytes in the A and B tiles, constant over K
   uint32_t a_off[A_LD], b_off[B_LD];
+  bool b_gate[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = i * 32 + wave * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
     const int orow = row0 + min(r, rows - 1);
     const int arow = P.a_rows ? P.a_rows[orow] : orow;
-    a_off[i] = (uint32_t)((size_t)arow * P.lda + c * EPC);
+    a_off[i] = (uint32_t)(((size_t)arow * P.lda + c * EPC) * sizeof(T));
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int r = i * 32 + wave * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const bool gate = SWIGLU && (i >= B_LD / 2);
-    const int brow = SWIGLU ? nt * (BN / 2) + (gate ? r - BN / 2 : r) : nt * BN + r;
-    b_off[i] = (uint32_t)((size_t)brow * P.ldb + c * EPC);
+    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const bool gate = SWIGLU && r >= BN / 2;   // the same for the whole wave
+    b_gate[i] = gate;
+    // rows past N (a ragged last column tile) re-read row N-1; their columns are not stored
+    const int brow = min(SWIGLU ? nt * (BN / 2) + (gate ? r - BN / 2 : r) : nt * BN + r, P.N - 1);
+    b_off[i] = (uint32_t)(((size_t)brow * P.ldb + c * EPC) * sizeof(T));
   }
 
   const int nk = P.K / BK;
-  auto issue_stage = [&](int kt, int buf) {
-    const int64_t k0 = (int64_t)kt * BK;
-    const int64_t seg = k0 / P.k_seg;
-    const int64_t boff = seg * P.k_seg_stride + (k0 - seg * P.k_seg);
-    uint8_t* sa = smem + buf * STAGE + wave * 8 * kRowB;
-    uint8_t* sb = smem + buf * STAGE + A_BYTES + wave * 8 * kRowB;
+  // Source positions of the next stage to load: K offset into A, and into B (whose K axis may be
+  // split into segments of k_seg elements placed k_seg_stride apart). Stages are issued in order.
+  const int k_seg = (int)P.k_seg;
+  const int64_t k_skip = P.k_seg_stride - P.k_seg;
+  int64_t a_k = 0, b_k = 0;
+  int b_within = 0;
+  const uint32_t wave_off = (uint32_t)(wave * kRowsPerLoad * kRowB);
+  auto issue_stage = [&](uint32_t stage) {
+    const uint32_t sa = stage + wave_off;
+    const uint32_t sb = stage + A_BYTES + wave_off;
+    const T* a_base = Ab + a_k;
+    const T* b_base = Bb + b_k;
+    const T* b3_base = SWIGLU ? B3b + b_k : nullptr;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) gload_lds16(Ab + k0 + a_off[i], sa + i * 32 * kRowB);
+    for (int i = 0; i < A_LD; ++i) gload_lds16(a_base, a_off[i], sa + i * kRowsPerLoad * kWaves * kRowB);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const bool gate = SWIGLU && (i >= B_LD / 2);
-      gload_lds16((gate ? B3b : Bb) + boff + b_off[i], sb + i * 32 * kRowB);
+    for (int i = 0; i < B_LD; ++i)
+      gload_lds16(b_gate[i] ? b3_base : b_base, b_off[i], sb + i * kRowsPerLoad * kWaves * kRowB);
+    a_k += BK;
+    b_k += BK;
+    b_within += BK;
+    if (b_within == k_seg) {
+      b_within = 0;
+      b_k += k_skip;
     }
   };
 
@@ -198,27 +265,75 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 #pragma unroll
     for (int j = 0; j < MJ; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue_stage(0, 0);
   const int fr = lane & 15, fg = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    wait_vmem();
-    __syncthreads();                       // stage kt is in LDS; stage kt-1's buffer is free
-    if (kt + 1 < nk) issue_stage(kt + 1, (kt + 1) & 1);
-    const uint8_t* sa = smem + (kt & 1) * STAGE;
-    const uint8_t* sb = sa + A_BYTES;
+  // Fragments of one K step: f[0..MJ) token rows (operand Q), f[MJ..) weight rows (operand P).
+  auto read_frags = [&](const uint8_t* stage, uint4 (&f)[NF]) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ks * 4 + fg;
-      uint4 af[MJ], bfr[NI];
+    for (int j = 0; j < MJ; ++j) f[j] = *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + j * 16 + fr, fg));
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) af[j] = *reinterpret_cast<const uint4*>(sa + swz(wm * 128 + j * 16 + fr, ch));
-#pragma unroll
-      for (int i = 0; i < NI; ++i) bfr[i] = *reinterpret_cast<const uint4*>(sb + swz(brow_of(i) + fr, ch));
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < MJ; ++j) acc[i][j] = mfma16(bfr[i], af[j], acc[i][j], T());
+    for (int i = 0; i < NI; ++i)
+      f[MJ + i] = *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(i) + fr, fg));
+  };
+  // Wait for stage s, with the `ahead` stages issued after it allowed to stay in flight, and for all
+  // LDS reads; then synchronise: stage s is complete for every wave.
+  auto sync_stage = [&](int ahead) {
+    if (ahead >= 2) wait_vmem<2 * LPS>();
+    else if (ahead == 1) wait_vmem<LPS>();
+    else wait_vmem<0>();
+    ring_barrier();
+  };
+
+  // Software pipeline: while the MFMAs of step kt run on registers fa/fb, the fragments of step
+  // kt + 1 are read from LDS into the other set, and stages kt + 2 .. kt + 3 are in flight from
+  // global memory into the LDS ring.
+  uint4 fa[NF], fb[NF];
+  issue_stage(lds_addr(smem0));
+  if (nk > 1) issue_stage(lds_addr(smem1));
+  if (nk > 2) issue_stage(lds_addr(smem2));
+  sync_stage(min(2, nk - 1));               // stages 1 and 2 may still be in flight
+  read_frags(smem0, fa);
+  // The fragment reads of the next step are spread between the MFMAs of this one: issued as one
+  // block they fill the LDS command queue and stall the wave (issue is in order) before its first
+  // MFMA. Read q goes right before MFMA (q * NM) / NF; sched_group_barrier pins that order. The
+  // body is generated by compile-time recursion so that every accumulator index is a constant.
+  constexpr int NM = NI * MJ;   // MFMAs per step
+  auto read_frag = [&](const uint8_t* stage, auto Qc) -> uint4 {
+    constexpr int q = decltype(Qc)::value;
+    if constexpr (q < MJ) return *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + q * 16 + fr, fg));
+    else return *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(q - MJ) + fr, fg));
+  };
+  auto body = [&](auto self, auto Mc, const uint8_t* next, uint4 (&cur)[NF], uint4 (&nxt)[NF]) -> void {
+    constexpr int m = decltype(Mc)::value;
+    if constexpr (m < NM) {
+      constexpr int q = (m * NF + NM - 1) / NM;   // the read that belongs right before MFMA m, if any
+      if constexpr (q < NF && (q * NM) / NF == m) nxt[q] = read_frag(next, std::integral_constant<int, q>{});
+      constexpr int i = m / MJ, j = m % MJ;
+      acc[i][j] = mfma16(cur[MJ + i], cur[j], acc[i][j], T());
+      self(self, std::integral_constant<int, m + 1>{}, next, cur, nxt);
     }
+  };
+  // step kt: sync on stage kt + 1, refill the slot of stage kt - 1 with stage kt + 3, read stage
+  // kt + 1 while multiplying stage kt.
+  auto step = [&](int kt, const uint8_t* next, uint32_t refill, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
+    // cur was read during the previous step; waiting here (and not only inside the branch) leaves
+    // no LDS read pending on either path.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    if (kt + 1 < nk) {
+      // issued so far: stages up to kt + 2 (stage kt + 3 is issued below)
+      sync_stage(min(1, nk - 2 - kt));
+      if (kt + 3 < nk) issue_stage(refill);
+    }
+    // One MFMA sequence on every path (two would make the accumulators merge at a join). On the
+    // last step the reads of `next` land in fragments nobody uses; `next` is always a valid stage.
+    body(body, std::integral_constant<int, 0>{}, next, cur, nxt);
+    sched_interleave<NM, NF>();
+  };
+  const uint32_t l0 = lds_addr(smem0), l1 = lds_addr(smem1), l2 = lds_addr(smem2), l3 = lds_addr(smem3);
+  for (int kt = 0; kt < nk; kt += kStages) {
+    step(kt, smem1, l3, fa, fb);
+    if (kt + 1 < nk) step(kt + 1, smem2, l0, fb, fa);
+    if (kt + 2 < nk) step(kt + 2, smem3, l1, fa, fb);
+    if (kt + 3 < nk) step(kt + 3, smem0, l2, fb, fa);
   }
 
   // ---- epilogue: lane holds rows (m) = wm*128 + j*16 + fr, columns 4*fg + t of n-subtile i
@@ -242,6 +357,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
           else h[t] = gelu_erf(u);
         }
         const int n = SWIGLU ? nt * (BN / 2) + wn * (BN / 4) + i * 16 + 4 * fg : nt * BN + wn * (BN / 2) + i * 16 + 4 * fg;
+        if (n >= P.N) continue;
         if (sizeof(T) == 2) {
           uint2 v;
           v.x = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
@@ -256,6 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int n = nt * BN + wn * (BN / 2) + i * 16 + 4 * fg;
+        if (n >= P.N) continue;
         *reinterpret_cast<float4*>(crow + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
     }
@@ -264,14 +381,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 
 static int out_cols_per_tile(int kind, int act, int BN) { return (kind == GEMM_UP && act == ACT_SWIGLU) ? BN / 2 : BN; }
 
+// The 256-row weight tile keeps LDS reads per MFMA lower than the 128-row one, so it is used
+// unless padding N up to whole tiles would waste more than 1/8 of the work.
 static int pick_bn(int kind, int act, int N) {
-  if (N % out_cols_per_tile(kind, act, 256) == 0) return 256;
-  if (N % out_cols_per_tile(kind, act, 128) == 0) return 128;
-  return 0;
+  if (N <= 0 || N % 64 != 0) return 0;
+  const int c256 = out_cols_per_tile(kind, act, 256);
+  const int64_t padded = ((int64_t)N + c256 - 1) / c256 * c256;
+  if (padded * 8 <= (int64_t)N * 9) return 256;
+  return 128;
 }
 
 bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K) {
-  const int bk = dtype == 0 ? 64 : 32;
+  const int bk = kRowB / (dtype == 0 ? 2 : 4);
   return N > 0 && K > 0 && K % bk == 0 && pick_bn(kind, act, N) != 0;
 }
 
@@ -310,7 +431,8 @@ hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* 
   int64_t total = 0;
   for (int i = 0; i < nprob; ++i) {
     if (pick_bn(kind, act, probs[i].N) != bn) return hipErrorInvalidValue;
-    const int32_t tiles_n = probs[i].N / out_cols_per_tile(kind, act, bn);
+    const int c = out_cols_per_tile(kind, act, bn);
+    const int32_t tiles_n = (probs[i].N + c - 1) / c;
     int64_t mt;
     if (probs[i].offsets) mt = (rows_ub[i] + kBM - 1) / kBM + probs[i].G;   // sum of ceil() over groups
     else mt = (int64_t)probs[i].G * ((probs[i].M_uni + kBM - 1) / kBM);

@@ -89,16 +89,20 @@ def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what="", base
     nref = np.linalg.norm(y_ref)
     rel = np.linalg.norm(diff) / max(nref, 1e-30)
     allow = 0.0
+    scale = 1.0
     if base_gpu is not None:
-        diff = (y_gpu - np.asarray(base_gpu, np.float64)) - (y_ref - np.asarray(base_ref, np.float64))
+        inc_ref = y_ref - np.asarray(base_ref, np.float64)
+        diff = (y_gpu - np.asarray(base_gpu, np.float64)) - inc_ref
         allow = 2.0 ** -8 * np.abs(y_ref)
+        # the absolute bound is for unit-RMS layer outputs; deeper stack layers add larger increments
+        scale = max(1.0, float(np.sqrt(np.mean(inc_ref ** 2))))
     excess = np.abs(diff) - allow
     mx = excess.max() if diff.size else 0.0
     if dtype == "bf16":
         tag = "max-abs" if base_gpu is None else "max-abs of increment beyond half-ulp"
-        say(f"  {what}: rel-L2 {rel:.3e} (<= {BF16_REL_L2}), {tag} {mx:.3e} (<= {BF16_MAX_ABS})")
+        say(f"  {what}: rel-L2 {rel:.3e} (<= {BF16_REL_L2}), {tag} {mx:.3e} (<= {BF16_MAX_ABS} x {scale:.2f})")
         assert rel <= BF16_REL_L2, f"{what}: rel-L2 {rel}"
-        assert mx <= BF16_MAX_ABS, f"{what}: max-abs {mx}"
+        assert mx <= BF16_MAX_ABS * scale, f"{what}: max-abs {mx}"
     else:
         mx = np.abs(diff).max() if diff.size else 0.0
         scale = max(np.abs(y_ref).max(), 1e-30)
@@ -114,7 +118,10 @@ def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what="", base
 # valid choices; everywhere else the decisions must match exactly.
 
 def reconcile_tc(spec, L64, rt, idx_gpu, reuse_gpu=None, eps=1e-4, max_frac=1e-3):
+    """eps: the decision margin below which both choices are accepted, a scalar or one per token
+    (a layer deep in a stack sees inputs that differ by rounding from the oracle's)."""
     idx_gpu = np.asarray(idx_gpu, np.int64)
+    eps = np.broadcast_to(np.asarray(eps, np.float64), (L64.shape[0],))
     P = rt["P"]
     k = idx_gpu.shape[1]
     keys = L64
@@ -134,10 +141,10 @@ def reconcile_tc(spec, L64, rt, idx_gpu, reuse_gpu=None, eps=1e-4, max_frac=1e-3
         # every chosen GPU expert must be within eps of the k-th oracle key, and the order flip
         # must be between near-equal keys
         g = keys[s, idx_gpu[s]]
-        assert np.all(g >= kth[s] - eps), f"token {s}: GPU took {idx_gpu[s]}, oracle {rt['idx'][s]}"
+        assert np.all(g >= kth[s] - eps[s]), f"token {s}: GPU took {idx_gpu[s]}, oracle {rt['idx'][s]}"
         if not same[s]:
-            assert kth[s] - nxt[s] < eps, f"token {s}: set differs without a near tie"
-        assert np.all(np.diff(g) <= eps), f"token {s}: GPU slot order not by key"
+            assert kth[s] - nxt[s] < eps[s], f"token {s}: set differs without a near tie"
+        assert np.all(np.diff(g) <= eps[s]), f"token {s}: GPU slot order not by key"
         n_fix += 1
     if len(bad):
         rt = dict(rt)

@@ -14,14 +14,15 @@ from synth import WORKLOADS, gen_layer_inputs, gen_tensor
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_rt(spec, L64, got_rb, reuse=True):
+def _oracle_rt(spec, L64, got_rb, reuse=True, eps=1e-4, max_frac=1e-3):
     rt = orc.route(spec, L=L64)
     g = {k: v.cpu().numpy() for k, v in got_rb.tensors.items()}
     if spec.mode == "ec":
         return reconcile_ec(spec, rt, g["row_token"], rt["C"])
     if spec.mode == "des":
         rt = reconcile_des(spec, rt, g["core"][: spec.m_core], L64)
-    return reconcile_tc(spec, L64, rt, g["topk_idx"], g["reuse"] if (reuse and spec.reuse_tau > 0) else None)
+    return reconcile_tc(spec, L64, rt, g["topk_idx"], g["reuse"] if (reuse and spec.reuse_tau > 0) else None,
+                        eps=eps, max_frac=max_frac)
 
 
 def _layer_case(spec, seed=0, flags=0, with_cache=False, residual=False):
@@ -106,29 +107,51 @@ def test_identity_only_is_exact():
 
 
 def test_mmoe_stack_reduced():
+    """Four MoE++ layers with gate residual on a residual stream.
+
+    Per layer, both sides start from the same inputs: the oracle's bf16 stream h_l and its logits
+    L_{l-1} rounded to fp32 go to the GPU layer, so each layer is checked on its own. Then the GPU
+    runs the whole stack on its own outputs and the final stream is compared end to end."""
     spec = WORKLOADS["mmoe"].replace(S=600)
     say(f"stack {spec.name}: S={spec.S} layers={spec.n_layers}")
     inp = gen_layer_inputs(spec)
-    h_dev = dev_tensor(inp.x, inp.bits["x"], "bf16")
     h64 = inp.x.astype(np.float64)
-    prev_dev = None
-    prev64 = None
+    prev32 = None
+    desc = moe.desc_from_spec(spec)
+    ws = moe.workspace(desc)
+    wts = [upload_layer(inp, layer) for layer in range(spec.n_layers)]
     for layer in range(spec.n_layers):
-        wt = upload_layer(inp, layer)
-        desc = moe.desc_from_spec(spec)
+        h_dev = dev_tensor(h64.astype(np.float32), None, "bf16")
+        prev_dev = None if prev32 is None else torch.from_numpy(prev32).cuda()
         rb = moe.alloc_routing(desc)
-        ws = moe.workspace(desc)
         y = torch.empty_like(h_dev)
         logits = torch.empty((spec.S, spec.E_routed), dtype=torch.float32, device="cuda")
-        moe.moe_layer_forward(desc, h_dev, moe.weights_struct(wt), prev_dev, logits, rb.struct, None, h_dev, y, ws)
+        moe.moe_layer_forward(desc, h_dev, moe.weights_struct(wts[layer]), prev_dev, logits, rb.struct, None, h_dev,
+                              y, ws)
         torch.cuda.synchronize()
+        prev64 = None if prev32 is None else prev32.astype(np.float64)
         L64 = orc.router_logits(h64, inp.w_router[layer], prev64)
+        assert np.allclose(to_np(logits), L64, atol=2e-5 * max(1.0, np.abs(L64).max()))
         rt = _oracle_rt(spec, L64, rb)
         ref = orc.layer_forward(spec, inp, h64, layer=layer, prev_logits=prev64, residual=h64, rt=rt)
-        assert_close(to_np(y), ref["y"], "bf16", f"layer {layer}", base_gpu=to_np(h_dev), base_ref=h64)
+        assert_close(to_np(y), ref["y"], "bf16", f"layer {layer}", base_gpu=h64, base_ref=h64)
         h64 = orc.bf16_round(ref["y"])
-        prev64 = ref["logits"]
+        prev32 = ref["logits"].astype(np.float32)
+    # end to end on the GPU's own stream
+    h_dev = dev_tensor(inp.x, inp.bits["x"], "bf16")
+    prev_dev = None
+    for layer in range(spec.n_layers):
+        y = torch.empty_like(h_dev)
+        logits = torch.empty((spec.S, spec.E_routed), dtype=torch.float32, device="cuda")
+        moe.moe_layer_forward(desc, h_dev, moe.weights_struct(wts[layer]), prev_dev, logits, None, None, h_dev, y, ws)
         h_dev, prev_dev = y, logits
+    torch.cuda.synchronize()
+    got = to_np(h_dev)
+    rel = np.linalg.norm(got - h64) / np.linalg.norm(h64)
+    say(f"  end-to-end stack rel-L2 {rel:.3e} (information; each layer is checked above)")
+    # Chained on its own stream, the GPU meets near-tied routing decisions in deeper layers that go
+    # the other way; each such token changes by O(|y|). Only a sanity bound is asserted here.
+    assert rel <= 5e-2
 
 
 def test_four_call_path_matches_layer_forward():
