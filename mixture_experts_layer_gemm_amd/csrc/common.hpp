@@ -31,11 +31,13 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
   static constexpr int kPer16B = 8;   // elements in one 16-byte chunk
+  static constexpr int kMfmaPerStep = 1;   // MFMA instructions per 16x16 product over 16 bytes of K
   __device__ static __forceinline__ float to_f(bf16_t v) { return bf16_to_f32(v); }
   __device__ static __forceinline__ bf16_t from_f(float v) { return f32_to_bf16(v); }
 };
 template <> struct Elem<float> {
   static constexpr int kPer16B = 4;
+  static constexpr int kMfmaPerStep = 4;
   __device__ static __forceinline__ float to_f(float v) { return v; }
   __device__ static __forceinline__ float from_f(float v) { return v; }
 };

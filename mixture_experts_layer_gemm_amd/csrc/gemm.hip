@@ -139,16 +139,38 @@ __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& 
   return g >= 0;
 }
 
-// Scheduling pattern for the K step: NF times (one LDS read, then its share of the NM MFMAs).
-template <int NM, int NF, int Q = 0>
-__device__ __forceinline__ void sched_interleave() {
-  if constexpr (Q < NF) {
-    constexpr int cnt = (Q + 1 < NF ? ((Q + 1) * NM) / NF : NM) - (Q * NM) / NF;
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                  // DS read
-    if constexpr (cnt > 0) __builtin_amdgcn_sched_group_barrier(0x008, cnt, 0);   // MFMA
-    sched_interleave<NM, NF, Q + 1>();
+// Placement of the work of one K step: NM MFMAs; NF LDS reads, read q right before MFMA
+// (q * NM) / NF; LPS global->LDS loads, load d right before MFMA (d * NM) / LPS. An "MFMA" here is
+// one 16x16 product step, MPC instructions. region<M0, M1>() pins the order of the LDS reads and
+// MFMAs of MFMAs [M0, M1) (loads bound the regions).
+template <int NM, int NF, int LPS, int MPC>
+struct step_sched {
+  static constexpr int load_pos(int d) { return d < 0 ? 0 : (d * NM) / LPS; }
+  static constexpr int load_at(int m) {
+    for (int d = 0; d < LPS; ++d)
+      if (load_pos(d) == m) return d;
+    return -1;
   }
-}
+  static constexpr bool read_at(int m) {
+    const int q = (m * NF + NM - 1) / NM;
+    return q < NF && (q * NM) / NF == m;
+  }
+  // MFMAs from m up to (not including) the next read position or m1
+  static constexpr int run(int m, int m1) {
+    int e = m + 1;
+    while (e < m1 && !read_at(e)) ++e;
+    return e - m;
+  }
+  template <int M0, int M1>
+  __device__ static __forceinline__ void region() {
+    if constexpr (M0 < M1) {
+      constexpr int n = run(M0, M1);
+      if constexpr (read_at(M0)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, n * MPC, 0);                       // MFMA
+      region<M0 + n, M1>();
+    }
+  }
+};
 
 template <typename T, int KIND, int ACT, int BN>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
@@ -224,23 +246,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 
   const int nk = P.K / BK;
   // Source positions of the next stage to load: K offset into A, and into B (whose K axis may be
-  // split into segments of k_seg elements placed k_seg_stride apart). Stages are issued in order.
+  // split into segments of k_seg elements placed k_seg_stride apart). Stages are issued in order,
+  // one per K step; stages past the end re-load stage 0 (valid memory, never read).
   const int k_seg = (int)P.k_seg;
   const int64_t k_skip = P.k_seg_stride - P.k_seg;
   int64_t a_k = 0, b_k = 0;
-  int b_within = 0;
+  int b_within = 0, issued = 0;
   const uint32_t wave_off = (uint32_t)(wave * kRowsPerLoad * kRowB);
-  auto issue_stage = [&](uint32_t stage) {
-    const uint32_t sa = stage + wave_off;
-    const uint32_t sb = stage + A_BYTES + wave_off;
-    const T* a_base = Ab + a_k;
-    const T* b_base = Bb + b_k;
-    const T* b3_base = SWIGLU ? B3b + b_k : nullptr;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) gload_lds16(a_base, a_off[i], sa + i * kRowsPerLoad * kWaves * kRowB);
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i)
-      gload_lds16(b_gate[i] ? b3_base : b_base, b_off[i], sb + i * kRowsPerLoad * kWaves * kRowB);
+  struct Dma {
+    const T* a;
+    const T* b;
+    const T* b3;
+    uint32_t lds;
+  };
+  auto next_dma = [&](uint32_t stage) -> Dma {
+    Dma d;
+    const bool live = issued < nk;
+    d.a = Ab + (live ? a_k : 0);
+    d.b = Bb + (live ? b_k : 0);
+    d.b3 = SWIGLU ? B3b + (live ? b_k : 0) : nullptr;
+    d.lds = stage + wave_off;
+    ++issued;
     a_k += BK;
     b_k += BK;
     b_within += BK;
@@ -248,6 +274,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
       b_within = 0;
       b_k += k_skip;
     }
+    return d;
+  };
+  // load instruction q (0..LPS) of a stage: A loads first, then B
+  auto dma_one = [&](const Dma& d, auto Qc) {
+    constexpr int q = decltype(Qc)::value;
+    if constexpr (q < A_LD) {
+      gload_lds16(d.a, a_off[q], d.lds + q * kRowsPerLoad * kWaves * kRowB);
+    } else {
+      constexpr int i = q - A_LD;
+      gload_lds16(b_gate[i] ? d.b3 : d.b, b_off[i], d.lds + A_BYTES + i * kRowsPerLoad * kWaves * kRowB);
+    }
+  };
+  auto issue_all = [&](const Dma& d) {
+    dma_one(d, std::integral_constant<int, 0>{});
+    if constexpr (LPS > 1) dma_one(d, std::integral_constant<int, 1>{});
+    if constexpr (LPS > 2) dma_one(d, std::integral_constant<int, 2>{});
+    if constexpr (LPS > 3) dma_one(d, std::integral_constant<int, 3>{});
+    if constexpr (LPS > 4) dma_one(d, std::integral_constant<int, 4>{});
+    if constexpr (LPS > 5) dma_one(d, std::integral_constant<int, 5>{});
+    if constexpr (LPS > 6) dma_one(d, std::integral_constant<int, 6>{});
+    if constexpr (LPS > 7) dma_one(d, std::integral_constant<int, 7>{});
+    static_assert(LPS <= 8, "at most 8 loads per stage");
   };
 
   // B-tile row of n-subtile i for this wave.
@@ -274,67 +322,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     for (int i = 0; i < NI; ++i)
       f[MJ + i] = *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(i) + fr, fg));
   };
-  // Wait for stage s, with the `ahead` stages issued after it allowed to stay in flight, and for all
-  // LDS reads; then synchronise: stage s is complete for every wave.
-  auto sync_stage = [&](int ahead) {
-    if (ahead >= 2) wait_vmem<2 * LPS>();
-    else if (ahead == 1) wait_vmem<LPS>();
-    else wait_vmem<0>();
-    ring_barrier();
-  };
 
-  // Software pipeline: while the MFMAs of step kt run on registers fa/fb, the fragments of step
-  // kt + 1 are read from LDS into the other set, and stages kt + 2 .. kt + 3 are in flight from
-  // global memory into the LDS ring.
-  uint4 fa[NF], fb[NF];
-  issue_stage(lds_addr(smem0));
-  if (nk > 1) issue_stage(lds_addr(smem1));
-  if (nk > 2) issue_stage(lds_addr(smem2));
-  sync_stage(min(2, nk - 1));               // stages 1 and 2 may still be in flight
-  read_frags(smem0, fa);
-  // The fragment reads of the next step are spread between the MFMAs of this one: issued as one
-  // block they fill the LDS command queue and stall the wave (issue is in order) before its first
-  // MFMA. Read q goes right before MFMA (q * NM) / NF; sched_group_barrier pins that order. The
-  // body is generated by compile-time recursion so that every accumulator index is a constant.
+  // One K step t, after the barrier: MFMAs on the fragments of stage t (cur) with, spread between
+  // them, the LDS reads of stage t + 1 (into nxt) and the loads of stage t + 4 (into the LDS slot
+  // of stage t, free once every wave has passed the barrier). Issued as blocks, the LDS reads would
+  // fill the LDS queue and the loads the memory queue, stalling the wave before its MFMAs (issue is
+  // in order). Loads are inline assembly, which the scheduler does not move, so the step is a chain
+  // of regions separated by loads, each with its own sched_group_barrier pattern. The body is
+  // generated by compile-time recursion so that every accumulator index is a constant.
   constexpr int NM = NI * MJ;   // MFMAs per step
+  using SS = step_sched<NM, NF, LPS, Elem<T>::kMfmaPerStep>;
   auto read_frag = [&](const uint8_t* stage, auto Qc) -> uint4 {
     constexpr int q = decltype(Qc)::value;
     if constexpr (q < MJ) return *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + q * 16 + fr, fg));
     else return *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(q - MJ) + fr, fg));
   };
-  auto body = [&](auto self, auto Mc, const uint8_t* next, uint4 (&cur)[NF], uint4 (&nxt)[NF]) -> void {
+  auto body = [&](auto self, auto Mc, const uint8_t* next, const Dma& dma, uint4 (&cur)[NF],
+                  uint4 (&nxt)[NF]) -> void {
     constexpr int m = decltype(Mc)::value;
     if constexpr (m < NM) {
+      constexpr int d = SS::load_at(m);
+      if constexpr (d >= 0) {
+        SS::template region<SS::load_pos(d - 1), m>();
+        dma_one(dma, std::integral_constant<int, d>{});
+      }
       constexpr int q = (m * NF + NM - 1) / NM;   // the read that belongs right before MFMA m, if any
       if constexpr (q < NF && (q * NM) / NF == m) nxt[q] = read_frag(next, std::integral_constant<int, q>{});
       constexpr int i = m / MJ, j = m % MJ;
       acc[i][j] = mfma16(cur[MJ + i], cur[j], acc[i][j], T());
-      self(self, std::integral_constant<int, m + 1>{}, next, cur, nxt);
+      self(self, std::integral_constant<int, m + 1>{}, next, dma, cur, nxt);
+    } else {
+      SS::template region<SS::load_pos(LPS - 1), NM>();
     }
   };
-  // step kt: sync on stage kt + 1, refill the slot of stage kt - 1 with stage kt + 3, read stage
-  // kt + 1 while multiplying stage kt.
-  auto step = [&](int kt, const uint8_t* next, uint32_t refill, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
-    // cur was read during the previous step; waiting here (and not only inside the branch) leaves
-    // no LDS read pending on either path.
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-    if (kt + 1 < nk) {
-      // issued so far: stages up to kt + 2 (stage kt + 3 is issued below)
-      sync_stage(min(1, nk - 2 - kt));
-      if (kt + 3 < nk) issue_stage(refill);
-    }
-    // One MFMA sequence on every path (two would make the accumulators merge at a join). On the
-    // last step the reads of `next` land in fragments nobody uses; `next` is always a valid stage.
-    body(body, std::integral_constant<int, 0>{}, next, cur, nxt);
-    sched_interleave<NM, NF>();
+  // step t: wait for stage t + 1 (stages t + 2, t + 3 may stay in flight), synchronise, then the body.
+  auto step = [&](const uint8_t* next, uint32_t refill, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): cur is in registers
+    wait_vmem<2 * LPS>();
+    ring_barrier();
+    const Dma dma = next_dma(refill);
+    body(body, std::integral_constant<int, 0>{}, next, dma, cur, nxt);
   };
+
+  uint4 fa[NF], fb[NF];
   const uint32_t l0 = lds_addr(smem0), l1 = lds_addr(smem1), l2 = lds_addr(smem2), l3 = lds_addr(smem3);
+  issue_all(next_dma(l0));
+  issue_all(next_dma(l1));
+  issue_all(next_dma(l2));
+  issue_all(next_dma(l3));
+  wait_vmem<3 * LPS>();
+  ring_barrier();
+  read_frags(smem0, fa);
   for (int kt = 0; kt < nk; kt += kStages) {
-    step(kt, smem1, l3, fa, fb);
-    if (kt + 1 < nk) step(kt + 1, smem2, l0, fb, fa);
-    if (kt + 2 < nk) step(kt + 2, smem3, l1, fa, fb);
-    if (kt + 3 < nk) step(kt + 3, smem0, l2, fb, fa);
+    step(smem1, l0, fa, fb);
+    if (kt + 1 < nk) step(smem2, l1, fb, fa);
+    if (kt + 2 < nk) step(smem3, l2, fa, fb);
+    if (kt + 3 < nk) step(smem0, l3, fb, fa);
   }
+  wait_vmem<0>();   // no load into LDS may still be in flight when the workgroup ends
 
   // ---- epilogue: lane holds rows (m) = wm*128 + j*16 + fr, columns 4*fg + t of n-subtile i
   const int64_t col_base = (int64_t)g * P.c_gcol;
