@@ -40,10 +40,7 @@ constexpr int kGM = 8;              // m-tiles per sweep group
 struct GemmLaunch {
   GemmProblem p0, p1;
   int32_t tiles_n0, tiles_n1;
-  int32_t mt_ub0, mt_ub1;
-  int32_t tile_begin1;
-  int32_t nprob;
-  int32_t total_tiles;
+  int32_t slots0, slots1;   // workgroups per XCD reserved for each problem (from upper bounds)
 };
 
 // 16-byte chunk c (0..3) of tile row r sits at slot c ^ ((r >> 2) & 3): the 16-byte fragment reads
@@ -83,6 +80,22 @@ __device__ __forceinline__ void ring_barrier() {
 }
 
 // Map m-tile `mt` of problem P to (group, first row, rows). Returns false for a tile past the end.
+// Number of m-tiles of a problem: the sum over groups of ceil(rows / kBM). Called by one whole wave;
+// the result is wave-uniform.
+__device__ __forceinline__ int count_mtiles(const GemmProblem& P, int lane) {
+  if (!P.offsets) return P.G * ((P.M_uni + kBM - 1) / kBM);
+  int total = 0;
+  for (int g0 = 0; g0 < P.G; g0 += 64) {
+    const int gi = g0 + lane;
+    int mts = 0;
+    if (gi < P.G) mts = (P.offsets[gi + 1] - P.offsets[gi] + kBM - 1) / kBM;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mts += __shfl_xor(mts, o, 64);
+    total += mts;
+  }
+  return total;
+}
+
 __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& g, int& row0, int& rows) {
   if (!P.offsets) {
     const int mpg = (P.M_uni + kBM - 1) / kBM;
@@ -194,18 +207,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem2[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem3[STAGE];
 
-  // ---- tile decode (XCD-contiguous renumbering)
-  const int nb = gridDim.x;
-  const int L = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
-  if (L >= args.total_tiles) return;
-  const bool second = args.nprob > 1 && L >= args.tile_begin1;
+  // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
+  // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
+  // contiguous chunks, one per XCD, swept as kGM m-tiles x all n-tiles, which keeps an expert's
+  // weight panels and token panels in one L2. An XCD runs its chunk of problem 0 (the one with the
+  // longer K, placed there by the host) and then its chunk of problem 1; workgroups beyond both
+  // chunks (the grid is sized from upper bounds on the row counts) exit at once.
+  __shared__ int s_mt[2];
+  if (threadIdx.x < 64) {
+    const int m0 = count_mtiles(args.p0, threadIdx.x);
+    const int m1 = args.slots1 ? count_mtiles(args.p1, threadIdx.x) : 0;
+    if (threadIdx.x == 0) {
+      s_mt[0] = m0;
+      s_mt[1] = m1;
+    }
+  }
+  __syncthreads();
+  const int live0 = s_mt[0] * args.tiles_n0, live1 = s_mt[1] * args.tiles_n1;
+  const int c0 = (live0 + 7) >> 3, c1 = (live1 + 7) >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const bool second = slot >= c0;
+  const int Lq = second ? xcd * c1 + (slot - c0) : xcd * c0 + slot;
+  if (second ? (slot - c0 >= c1 || Lq >= live1) : Lq >= live0) return;
   const GemmProblem P = second ? args.p1 : args.p0;   // a copy: kept in scalar registers
-  const int Lq = second ? L - args.tile_begin1 : L;
   const int tn = second ? args.tiles_n1 : args.tiles_n0;
-  const int mt_ub = second ? args.mt_ub1 : args.mt_ub0;
+  const int mt_live = second ? s_mt[1] : s_mt[0];
   const int grp = Lq / (kGM * tn);
   const int rem = Lq - grp * kGM * tn;
-  const int gsz = min(kGM, mt_ub - grp * kGM);
+  const int gsz = min(kGM, mt_live - grp * kGM);
   const int mt = grp * kGM + rem % gsz;
   const int nt = rem / gsz;
   int g, row0, rows;
@@ -471,32 +500,34 @@ hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* 
   if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
   const int bn = pick_bn(kind, act, probs[0].N);
   if (bn == 0) return hipErrorInvalidValue;
+  // the problem with the longer K goes first (see the tile decode in the kernel)
+  const int first = (nprob == 2 && probs[1].K > probs[0].K) ? 1 : 0;
   GemmLaunch la{};
-  la.nprob = nprob;
   int64_t total = 0;
-  for (int i = 0; i < nprob; ++i) {
+  for (int n = 0; n < nprob; ++n) {
+    const int i = n == 0 ? first : 1 - first;
     if (pick_bn(kind, act, probs[i].N) != bn) return hipErrorInvalidValue;
     const int c = out_cols_per_tile(kind, act, bn);
-    const int32_t tiles_n = (probs[i].N + c - 1) / c;
+    const int64_t tiles_n = (probs[i].N + c - 1) / c;
     int64_t mt;
     if (probs[i].offsets) mt = (rows_ub[i] + kBM - 1) / kBM + probs[i].G;   // sum of ceil() over groups
     else mt = (int64_t)probs[i].G * ((probs[i].M_uni + kBM - 1) / kBM);
-    if (i == 0) {
-      la.p0 = probs[0];
-      la.tiles_n0 = tiles_n;
-      la.mt_ub0 = (int32_t)mt;
+    const int64_t tiles = mt * tiles_n;
+    if (tiles > (int64_t)1 << 28) return hipErrorInvalidValue;
+    const int32_t slots = (int32_t)((tiles + 7) / 8);
+    if (n == 0) {
+      la.p0 = probs[i];
+      la.tiles_n0 = (int32_t)tiles_n;
+      la.slots0 = slots;
     } else {
-      la.p1 = probs[1];
-      la.tiles_n1 = tiles_n;
-      la.mt_ub1 = (int32_t)mt;
-      la.tile_begin1 = (int32_t)total;
+      la.p1 = probs[i];
+      la.tiles_n1 = (int32_t)tiles_n;
+      la.slots1 = slots;
     }
-    total += mt * tiles_n;
+    total += slots;
   }
   if (total == 0) return hipSuccess;
-  if (total > (int64_t)1 << 30) return hipErrorInvalidValue;
-  la.total_tiles = (int32_t)total;
-  const int grid = (int)((total + 7) / 8 * 8);
+  const int grid = (int)(8 * total);
   if (dtype == 0) launch_kind<bf16_t>(la, kind, act, bn, grid, st);
   else launch_kind<float>(la, kind, act, bn, grid, st);
   return hipGetLastError();
