@@ -50,7 +50,24 @@ def parse():
     ap.add_argument("--workload", default="dit_moe_xl", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (3 times): the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     return ap.parse_args()
+
+
+def calibrate_copy():
+    """A plain copy of known size. Under rocprofv3 --pmc its FETCH_SIZE and WRITE_SIZE per dispatch,
+    divided by 1 GiB read and 1 GiB written, give the factors that turn the counters into bytes."""
+    import torch
+
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 3}), flush=True)
 
 
 def sha256_of(path):
@@ -80,6 +97,9 @@ def main():
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
