@@ -69,6 +69,9 @@ typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1, MOE_DES_VOTE = 2 } m
 #define MOE_F_FORCE_TILED   0x8u  /* heavy experts on the tiled grouped GEMM (default: chosen from the
                                      expected rows per expert) */
 #define MOE_F_FORCE_STREAM  0x10u /* heavy experts on the weight-streaming kernel (few rows per expert) */
+#define MOE_F_ROUTE_MULTI   0x20u /* token choice / DES: always route and dispatch with the multi-launch
+                                     kernels (default: a small call, S * E_r <= 16384 and S * k <= 4096,
+                                     runs both in one workgroup; the results are identical) */
 
 /* Layer description [host]. Routed expert ids: [0, E_heavy) heavy, then n_identity identity,
  * n_zero zero and n_const constant experts; E_r = E_heavy + n_identity + n_zero + n_const. */

@@ -14,7 +14,7 @@ __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
     "MOE_BF16", "MOE_F32", "MOE_ACT_GELU", "MOE_ACT_GELU_TANH", "MOE_ACT_SWIGLU",
     "MOE_TOKEN_CHOICE", "MOE_EXPERT_CHOICE", "MOE_DES_VOTE",
-    "MOE_F_INPUT_PROBS", "MOE_F_SYNC_DEBUG", "MOE_F_FORCE_TILED", "MOE_F_FORCE_STREAM",
+    "MOE_F_INPUT_PROBS", "MOE_F_SYNC_DEBUG", "MOE_F_FORCE_TILED", "MOE_F_FORCE_STREAM", "MOE_F_ROUTE_MULTI",
     "MoeDesc", "MoeRouting", "MoeWeights", "MoeError", "MoeLibraryMissing",
     "lib", "lib_path", "EXPORTS",
     "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
@@ -26,6 +26,7 @@ MOE_BF16, MOE_F32 = 0, 1
 MOE_ACT_GELU, MOE_ACT_GELU_TANH, MOE_ACT_SWIGLU = 0, 1, 2
 MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE, MOE_DES_VOTE = 0, 1, 2
 MOE_F_INPUT_PROBS, MOE_F_SYNC_DEBUG, MOE_F_FORCE_TILED, MOE_F_FORCE_STREAM = 0x1, 0x4, 0x8, 0x10
+MOE_F_ROUTE_MULTI = 0x20
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
            "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_profile_entry")

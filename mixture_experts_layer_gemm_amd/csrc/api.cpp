@@ -47,7 +47,8 @@ namespace {
 
 using namespace moe;
 
-constexpr uint32_t kKnownFlags = MOE_F_INPUT_PROBS | MOE_F_SYNC_DEBUG | MOE_F_FORCE_TILED | MOE_F_FORCE_STREAM;
+constexpr uint32_t kKnownFlags =
+    MOE_F_INPUT_PROBS | MOE_F_SYNC_DEBUG | MOE_F_FORCE_TILED | MOE_F_FORCE_STREAM | MOE_F_ROUTE_MULTI;
 constexpr int kMaxExperts = 256;
 constexpr int kMaxK = 16;
 
@@ -122,7 +123,9 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
   if (d->E_heavy > 0) {
     const int64_t per_expert = p->R_max / std::max<int64_t>(1, std::min<int64_t>(
                                                                    d->E_heavy, d->mode == MOE_DES_VOTE ? d->m_core : d->E_heavy));
-    bool stream = per_expert <= 64;
+    const bool stream_ok = stream_gemm_supported(d->dtype, GEMM_UP, act, d->d_ff, d->d) &&
+                           stream_gemm_supported(d->dtype, GEMM_DOWN, act, d->d, d->d_ff);
+    bool stream = per_expert <= 64 && stream_ok;
     if (d->flags & MOE_F_FORCE_TILED) stream = false;
     if (d->flags & MOE_F_FORCE_STREAM) stream = true;
     p->streaming = stream;
@@ -290,12 +293,8 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
   a.reuse = r->reuse;
   a.votes = r->votes;
   a.core = r->core;
-  if (d->mode == MOE_DES_VOTE) {
-    a.k = d->k;   // the kernel applies min(k, m_core)
-    MOE_TRY(after_launch(launch_route_des(a, (float*)(w + p.o_filt), st), d, st));
-  } else {
-    MOE_TRY(after_launch(launch_route_topk(a, st), d, st));
-  }
+  const bool des = d->mode == MOE_DES_VOTE;
+  if (des) a.k = d->k;   // the kernels apply min(k, m_core)
   PermuteArgs q{};
   q.S = d->S;
   q.k = p.k_eff;
@@ -311,6 +310,10 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
   q.token_rows = r->token_rows;
   q.n_rows = r->n_rows;
   q.blk_cnt = (int32_t*)(w + p.o_blk);
+  // small calls (a decode block, a tiny batch): routing and dispatch in one workgroup
+  if (!(d->flags & MOE_F_ROUTE_MULTI) && route_small_supported(d->S, p.E_r, p.k_eff)) return after_launch(launch_route_small(a, q, des, st), d, st);
+  if (des) MOE_TRY(after_launch(launch_route_des(a, (float*)(w + p.o_filt), st), d, st));
+  else MOE_TRY(after_launch(launch_route_topk(a, st), d, st));
   return after_launch(launch_permute(q, st), d, st);
 }
 

@@ -66,6 +66,11 @@ struct PermuteArgs {
 int permute_num_blocks(int S, int k);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
+// Token choice or DES-Vote routing plus the dispatch of PermuteArgs, in one workgroup, for small
+// calls (route_small_supported). For DES, a.k is the requested k (min(k, m_core) is applied).
+bool route_small_supported(int S, int E_r, int k);
+hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st);
+
 // Expert choice.
 struct ECArgs {
   int S, E, C, input_probs;

@@ -13,77 +13,105 @@
 // logits (or given probabilities), compared exactly.
 #include <float.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace moe {
 
 // =============================================================================================
-// Router GEMM. One wave computes 16 tokens x all experts with 16x16 MFMA tiles: operand P = W_r
-// rows (16 experts), operand Q = x rows (16 tokens), so each lane ends with 4 consecutive experts
-// of one token. x is read once from HBM; W_r (a few KB to a few hundred KB) stays in cache.
-template <typename T>
-__global__ __launch_bounds__(64) void k_router(const T* __restrict__ x, const T* __restrict__ w,
-                                               const float* __restrict__ prev, float* __restrict__ logits,
-                                               int S, int d, int E) {
+// Router GEMM. A workgroup computes 16 tokens x (16 * ET) experts (grid.y covers the rest). Its W
+// waves split the K axis (wave w takes K steps w, w + W, ...), so each wave has only a few
+// dependent load rounds; the partial sums are then added in LDS in wave order (a fixed order:
+// results do not depend on timing). 16x16 MFMA tiles with operand P = W_r rows (16 experts) and
+// operand Q = x rows (16 tokens): each lane ends with 4 consecutive experts of one token. x is read
+// once from HBM per expert slice; W_r stays in cache.
+template <typename T, int ET>
+__global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const T* __restrict__ w,
+                                                 const float* __restrict__ prev, float* __restrict__ logits,
+                                                 int S, int d, int E) {
   constexpr int EPC = Elem<T>::kPer16B;
-  const int lane = threadIdx.x;
+  constexpr int STEP = 4 * EPC;   // K elements per MFMA step
+  constexpr int EW = ET * 16;     // experts per workgroup
+  extern __shared__ float s_part[];   // [W][16][EW]
+  const int W = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
   const int s0 = blockIdx.x * 16;
-  const int s = min(s0 + r, S - 1);
-  const T* xrow = x + (size_t)s * d + g * EPC;
-  const int e_tiles = (E + 15) >> 4;
-  for (int et0 = 0; et0 < e_tiles; et0 += 4) {
-    floatx4_t acc[4];
-    const T* wrow[4];
-    bool wok[4];
+  const int e0 = blockIdx.y * EW;
+  const T* xrow = x + (size_t)min(s0 + r, S - 1) * d + g * EPC;
+  const T* wrow[ET];
+  bool wok[ET];
+  floatx4_t acc[ET];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      const int e = (et0 + q) * 16 + r;
-      wok[q] = e < E;
-      wrow[q] = w + (size_t)min(e, E - 1) * d + g * EPC;
-    }
-#pragma unroll 4
-    for (int kk = 0; kk < d; kk += 4 * EPC) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xrow + kk);
+  for (int q = 0; q < ET; ++q) {
+    const int e = e0 + q * 16 + r;
+    wok[q] = e < E;
+    wrow[q] = w + (size_t)min(e, E - 1) * d + g * EPC;
+    acc[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const int nsteps = d / STEP;
+#pragma unroll 2
+  for (int t = wave; t < nsteps; t += W) {
+    const size_t kk = (size_t)t * STEP;
+    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + kk);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (et0 + q < e_tiles) {
-          uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
-          if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
-          acc[q] = mfma16(wv, xv, acc[q], T());
-        }
-      }
-    }
-    const int st = s0 + r;
-    if (st < S) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int e = (et0 + q) * 16 + 4 * g + t;
-          if (et0 + q < e_tiles && e < E) {
-            float v = acc[q][t];
-            if (prev) v += prev[(size_t)st * E + e];
-            logits[(size_t)st * E + e] = v;
-          }
-        }
-      }
+    for (int q = 0; q < ET; ++q) {
+      uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
+      if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
+      acc[q] = mfma16(wv, xv, acc[q], T());
     }
   }
+  float* mine = s_part + (size_t)wave * 16 * EW;
+#pragma unroll
+  for (int q = 0; q < ET; ++q)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) mine[r * EW + q * 16 + 4 * g + t] = acc[q][t];
+  __syncthreads();
+  const int ne = min(EW, E - e0);
+  for (int o = threadIdx.x; o < 16 * ne; o += blockDim.x) {
+    const int tr = o / ne, el = o - tr * ne;
+    const int st = s0 + tr, e = e0 + el;
+    if (st >= S) continue;
+    float v = 0.f;
+    for (int q = 0; q < W; ++q) v += s_part[((size_t)q * 16 + tr) * EW + el];
+    if (prev) v += prev[(size_t)st * E + e];
+    logits[(size_t)st * E + e] = v;
+  }
+}
+
+template <typename T, int ET>
+static void router_t(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
+                     hipStream_t st) {
+  constexpr int STEP = 4 * Elem<T>::kPer16B;
+  const int nsteps = d / STEP;
+  // about 4 K steps per wave; the partial sums of all waves fit in 64 KB of LDS
+  const int W = std::max(1, std::min({16, nsteps / 4, 64 / ET}));
+  const size_t lds = (size_t)W * 16 * ET * 16 * sizeof(float);
+  const dim3 grid((S + 15) / 16, (E + ET * 16 - 1) / (ET * 16));
+  auto kfn = k_router<T, ET>;
+  MOE_LAUNCH("router", kfn, grid, 64 * W, lds, st, (const T*)x, (const T*)w_router, prev, logits, S, d, E);
+}
+
+template <typename T>
+static void router_dt(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
+                      hipStream_t st) {
+  // few tokens: one 16-expert tile per workgroup, for more workgroups; many tokens: all experts in
+  // one workgroup, so x is read once
+  if (E <= 16 || S <= 1024) router_t<T, 1>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 32) router_t<T, 2>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 64) router_t<T, 4>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 128) router_t<T, 8>(x, w_router, prev, logits, S, d, E, st);
+  else router_t<T, 16>(x, w_router, prev, logits, S, d, E, st);
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits, int S,
                          int d, int E, hipStream_t st) {
-  const int blocks = (S + 15) / 16;
-  if (dtype == 0) {
-    auto kfn = k_router<bf16_t>;
-    MOE_LAUNCH("router", kfn, blocks, 64, 0, st, (const bf16_t*)x, (const bf16_t*)w_router, prev, logits, S, d, E);
-  } else {
-    auto kfn = k_router<float>;
-    MOE_LAUNCH("router", kfn, blocks, 64, 0, st, (const float*)x, (const float*)w_router, prev, logits, S, d, E);
-  }
+  if (S <= 0) return hipSuccess;
+  if (E < 1 || E > 256) return hipErrorInvalidValue;
+  if (dtype == 0) router_dt<bf16_t>(x, w_router, prev, logits, S, d, E, st);
+  else router_dt<float>(x, w_router, prev, logits, S, d, E, st);
   return hipGetLastError();
 }
 
@@ -464,6 +492,247 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
     auto kfn = k_perm_scatter;
     MOE_LAUNCH("perm_scatter", kfn, nblk, kPermThreads, 0, st, a, nbits);
   }
+  return hipGetLastError();
+}
+
+// =============================================================================================
+// Small calls (a DES decode block, a tiny batch): the whole routing of token choice or DES-Vote and
+// the counting-sort dispatch in one workgroup: one launch instead of four. Selections here are
+// computed by rank, one thread per (token, expert): rank(e) = the number of allowed experts o of the
+// token with key_o > key_e, or key_o == key_e and o < e; e is taken when rank(e) < k, into slot
+// rank(e). This is the same set and slot order as the iterative selection of k_route_topk /
+// k_route_des; votes are summed in the same order, and rows come out in the same (expert, token,
+// slot) order as the three permute kernels.
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / 64;
+constexpr int kSmallMaxSE = 8192;     // S * E_r: keys and probabilities kept in LDS
+constexpr int kSmallMaxPairs = 4096;  // S * k
+constexpr int kSmallMaxS = 2048;
+
+bool route_small_supported(int S, int E_r, int k) {
+  return S >= 1 && S <= kSmallMaxS && (int64_t)S * E_r <= kSmallMaxSE && (int64_t)S * k <= kSmallMaxPairs &&
+         E_r <= 256 && k <= kMaxK;
+}
+
+template <int LPT, int V, bool DES>
+__global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, PermuteArgs q) {
+  __shared__ float s_key[kSmallMaxSE];
+  __shared__ float s_p[kSmallMaxSE];
+  __shared__ uint8_t s_taken[DES ? kSmallMaxSE : 1];
+  __shared__ float s_votes[256];
+  __shared__ int s_incore[256];
+  __shared__ int s_idx[kSmallMaxPairs];
+  __shared__ float s_w[kSmallMaxPairs];
+  __shared__ uint8_t s_reuse[kSmallMaxS];
+  __shared__ int s_wcnt[kSmallWaves][256];
+  __shared__ int s_cnt[256], s_off[257], s_run[256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, E = a.E_r, SE = S * E;
+  const int kk = DES ? min(a.k, a.m_core) : a.k;
+
+  for (int i = tid; i < SE; i += kSmallThreads) s_key[i] = a.keys[i];
+  for (int e = tid; e < 256; e += kSmallThreads) {
+    s_cnt[e] = 0;
+    s_run[e] = 0;
+  }
+  for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) (&s_wcnt[0][0])[i] = 0;
+  __syncthreads();
+
+  // probabilities: LPT lanes per token (max-subtracted softmax, or the given probabilities)
+  constexpr int tpb = kSmallThreads / LPT;
+  const int sub = lane & (LPT - 1);
+  for (int base = 0; base < S; base += tpb) {
+    const int s = base + tid / LPT;
+    const bool live = s < S;
+    float key[V], p[V];
+    token_probs<LPT, V>(s_key + min(s, S - 1) * E, live, E, sub, a.input_probs, key, p);
+    float pm = 0.f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
+    pm = group_max<LPT>(pm);
+    if (live) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = sub + v * LPT;
+        if (e < E) s_p[s * E + e] = p[v];
+      }
+      if (sub == 0) s_reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
+    }
+  }
+  __syncthreads();
+  if (a.probs)
+    for (int i = tid; i < SE; i += kSmallThreads) a.probs[i] = s_p[i];
+  if (a.reuse)
+    for (int s = tid; s < S; s += kSmallThreads) a.reuse[s] = s_reuse[s];
+
+  // rank of (s, e) among the experts of s allowed by `ok`
+  auto rank_of = [&](int s, int e, auto ok) -> int {
+    const float* kr = s_key + s * E;
+    const float ke = kr[e];
+    int r = 0;
+#pragma unroll 8
+    for (int o = 0; o < E; ++o) {
+      const float ko = kr[o];
+      r += (ok(o) && (ko > ke || (ko == ke && o < e))) ? 1 : 0;
+    }
+    return r;
+  };
+
+  if constexpr (DES) {
+    // filter: the top-vote_k experts of each token keep their probability
+    for (int i = tid; i < SE; i += kSmallThreads) {
+      const int s = i / E, e = i - s * E;
+      s_taken[i] = rank_of(s, e, [](int) { return true; }) < a.vote_k ? 1 : 0;
+    }
+    __syncthreads();
+    // votes, summed over tokens in ascending order
+    for (int e = tid; e < E; e += kSmallThreads) {
+      float v = 0.f;
+#pragma unroll 8
+      for (int n = 0; n < S; ++n) v += s_taken[n * E + e] ? s_p[n * E + e] : 0.f;
+      s_votes[e] = v;
+      a.votes[e] = v;
+    }
+    __syncthreads();
+    // elect: rank under (vote desc, index asc)
+    for (int e = tid; e < E; e += kSmallThreads) {
+      const float ve = s_votes[e];
+      int rank = 0;
+#pragma unroll 8
+      for (int o = 0; o < E; ++o) {
+        const float vo = s_votes[o];
+        rank += (vo > ve || (vo == ve && o < e)) ? 1 : 0;
+      }
+      s_incore[e] = rank < a.m_core ? 1 : 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += kSmallThreads) {
+      if (s_incore[e]) {
+        int pos = 0;
+#pragma unroll 8
+        for (int o = 0; o < e; ++o) pos += s_incore[o];
+        a.core[pos] = e;
+      }
+    }
+  }
+
+  // selection: slot rank(e) of token s holds e when rank(e) < kk (inside the core for DES)
+  for (int i = tid; i < SE; i += kSmallThreads) {
+    const int s = i / E, e = i - s * E;
+    if (DES && !s_incore[e]) continue;
+    const int r = DES ? rank_of(s, e, [&](int o) { return s_incore[o] != 0; })
+                      : rank_of(s, e, [](int) { return true; });
+    if (r < kk) {
+      s_idx[s * kk + r] = e;
+      s_w[s * kk + r] = s_p[i];
+    }
+  }
+  __syncthreads();
+  // weights: p, or p over the sum of the chosen p in slot order
+  for (int s = tid; s < S; s += kSmallThreads) {
+    float denom = 1.f;
+    if (a.renorm) {
+      float t = 0.f;
+#pragma unroll 4
+      for (int j = 0; j < kk; ++j) t += s_w[s * kk + j];
+      denom = t;
+    }
+#pragma unroll 4
+    for (int j = 0; j < kk; ++j) {
+      const float wj = a.renorm ? s_w[s * kk + j] / denom : s_w[s * kk + j];
+      s_w[s * kk + j] = wj;
+      a.topk_idx[(size_t)s * kk + j] = s_idx[s * kk + j];
+      a.topk_w[(size_t)s * kk + j] = wj;
+    }
+  }
+  __syncthreads();
+
+  // dispatch: pair p = s * kk + j goes to a row when its expert is heavy and s does not reuse
+  const int P = S * kk;
+  const bool use_reuse = q.reuse != nullptr;
+  auto live_pair = [&](int p, int& e) -> bool {
+    if (p >= P) {
+      e = -1;
+      return false;
+    }
+    e = s_idx[p];
+    return e >= 0 && e < q.E_heavy && !(use_reuse && s_reuse[p / kk]);
+  };
+  for (int p = tid; p < P; p += kSmallThreads) {
+    int e;
+    if (live_pair(p, e)) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = tid; e <= E; e += kSmallThreads) {
+    int off = 0;
+#pragma unroll 8
+    for (int o = 0; o < e; ++o) off += o < q.E_heavy ? s_cnt[o] : 0;
+    s_off[e] = off;
+    q.offsets[e] = off;
+    if (e < E) q.counts[e] = e < q.E_heavy ? s_cnt[e] : 0;
+    if (e == E) *q.n_rows = off;
+  }
+  int nbits = 1;
+  while ((1 << nbits) <= q.E_heavy) ++nbits;
+  __syncthreads();
+  for (int r0 = 0; r0 < P; r0 += kSmallThreads) {
+    const int p = r0 + tid;
+    int e;
+    const bool ok = live_pair(p, e);
+    const int key = ok ? e : q.E_heavy;
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
+    }
+    const uint64_t lower = peers & lanemask_lt();
+    if (ok && lower == 0) s_wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (ok) {
+      int base = s_off[e] + s_run[e];
+      for (int o = 0; o < wave; ++o) base += s_wcnt[o][e];
+      const int row = base + __popcll(lower);
+      q.row_token[row] = p / kk;
+      q.row_w[row] = s_w[p];
+      q.token_rows[p] = row;
+    } else if (p < P) {
+      q.token_rows[p] = -1;
+    }
+    __syncthreads();
+    for (int i = tid; i < q.E_heavy; i += kSmallThreads) {
+      int add = 0;
+      for (int o = 0; o < kSmallWaves; ++o) {
+        add += s_wcnt[o][i];
+        s_wcnt[o][i] = 0;
+      }
+      s_run[i] += add;
+    }
+    __syncthreads();
+  }
+}
+
+template <int LPT, int V>
+static void route_small_t(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st) {
+  if (des) {
+    auto kfn = k_route_small<LPT, V, true>;
+    MOE_LAUNCH("route_small", kfn, 1, kSmallThreads, 0, st, a, q);
+  } else {
+    auto kfn = k_route_small<LPT, V, false>;
+    MOE_LAUNCH("route_small", kfn, 1, kSmallThreads, 0, st, a, q);
+  }
+}
+
+hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st) {
+  const int kk = des ? std::min(a.k, a.m_core) : a.k;
+  if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > 256) return hipErrorInvalidValue;
+  const int E = a.E_r;
+  if (E <= 8) route_small_t<8, 1>(a, q, des, st);
+  else if (E <= 16) route_small_t<16, 1>(a, q, des, st);
+  else if (E <= 32) route_small_t<32, 1>(a, q, des, st);
+  else if (E <= 64) route_small_t<64, 1>(a, q, des, st);
+  else if (E <= 128) route_small_t<64, 2>(a, q, des, st);
+  else route_small_t<64, 4>(a, q, des, st);
   return hipGetLastError();
 }
 

@@ -6,11 +6,13 @@
 // the block latency is dominated by b times the number of distinct experts loaded). This kernel
 // reads every weight byte of an active expert exactly once and keeps the MFMA work beside it.
 //
-// Layout: workgroup (x = 64-column slice, y = active-expert slot), 4 waves, each wave owns 16
-// output columns (16 weight rows; 32 for SwiGLU gate+up) and the full K. Weight rows are MFMA
-// operand P streamed straight from HBM (16-byte loads, 8 steps in flight); the expert's token rows
-// (operand Q, gathered through row_token) come from L2, 32 rows per pass. Experts with no rows are
-// skipped, so bytes = (active experts) x (weight bytes per expert).
+// Layout: workgroup (x = slice of 16 * G columns, y = active-expert slot) of G * SL waves. Wave w
+// owns 16 output columns (16 weight rows; 32 for SwiGLU gate+up): column group w % G, K slice
+// w / G. The slices take blocks of 4 MFMA steps (256 bytes of each row) in turn; each load
+// instruction reads 64 contiguous bytes of each of 16 rows. Weight rows are MFMA operand P,
+// streamed from HBM with non-temporal loads; the expert's token rows (operand Q, gathered through
+// row_token) come from L2, 32 rows per pass. The K slices are added in LDS in slice order.
+// Experts with no rows are skipped, so bytes = (active experts) x (weight bytes per expert).
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -37,10 +39,15 @@ __device__ __forceinline__ int locate_active(const GemmProblem& P, int slot) {
   return s_e;
 }
 
-template <typename T, int KIND, int ACT>
-__global__ __launch_bounds__(256) void k_stream_gemm(GemmProblem la_p) {
+// G (16-column groups) x SL (K slices) waves per workgroup
+template <typename T, int KIND, int ACT, int G, int SL>
+__global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
+  constexpr int COLS = 16 * G;
   constexpr int EPC = Elem<T>::kPer16B;
+  constexpr int KB = 16 * EPC;   // K elements per block (4 MFMA steps)
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
+  constexpr int NACC = SWIGLU ? 4 : 2;   // floatx4 accumulators per lane: 2 token groups (x gate)
+  __shared__ floatx4_t s_red[SL - 1][G][NACC][64];
   const GemmProblem& P = la_p;
   const int e = locate_active(P, blockIdx.y);
   if (e < 0) return;
@@ -48,100 +55,139 @@ __global__ __launch_bounds__(256) void k_stream_gemm(GemmProblem la_p) {
   const int cnt = P.offsets[e + 1] - beg;
   if (cnt <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = wave % G, ks = wave / G;
   const int fr = lane & 15, fg = lane >> 4;
-  const int n0 = blockIdx.x * 64 + wave * 16;
-  const T* wrow = (const T*)P.B + (size_t)e * P.b_gstride + (size_t)(n0 + fr) * P.ldb + fg * EPC;
-  const T* grow = SWIGLU ? (const T*)P.B3 + (size_t)e * P.b_gstride + (size_t)(n0 + fr) * P.ldb + fg * EPC : nullptr;
+  const int n0 = blockIdx.x * COLS + cg * 16;
+  const int lane_k = fg * EPC;   // this lane's 16 bytes inside each MFMA step
+  const T* wrow = (const T*)P.B + (size_t)e * P.b_gstride + (size_t)(n0 + fr) * P.ldb + lane_k;
+  const T* grow = SWIGLU ? (const T*)P.B3 + (size_t)e * P.b_gstride + (size_t)(n0 + fr) * P.ldb + lane_k : nullptr;
   const T* A = (const T*)P.A;
-  const int K = P.K;
+  const int nblk = P.K / KB;
   for (int t0 = 0; t0 < cnt; t0 += 32) {
     const T* xr[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int r = beg + min(t0 + j * 16 + fr, cnt - 1);
       const int src = P.a_rows ? P.a_rows[r] : r;
-      xr[j] = A + (size_t)src * P.lda + fg * EPC;
+      xr[j] = A + (size_t)src * P.lda + lane_k;
     }
-    floatx4_t acc[2], accg[2];
+    floatx4_t acc[NACC];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      accg[j] = acc[j];
-    }
+    for (int j = 0; j < NACC; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     const bool two = t0 + 16 < cnt;
-#pragma unroll 8
-    for (int k = 0; k < K; k += 4 * EPC) {
-      const uint4 w = load_nt16(wrow + k);
-      uint4 wg;
-      if (SWIGLU) wg = load_nt16(grow + k);
-      const uint4 x0 = *reinterpret_cast<const uint4*>(xr[0] + k);
-      acc[0] = mfma16(w, x0, acc[0], T());
-      if (SWIGLU) accg[0] = mfma16(wg, x0, accg[0], T());
+    for (int b = ks; b < nblk; b += SL) {
+      const size_t k = (size_t)b * KB;
+      uint4 w[4], wg[4], x0[4], x1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = load_nt16(wrow + k + i * 4 * EPC);
+      if (SWIGLU) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wg[i] = load_nt16(grow + k + i * 4 * EPC);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x0[i] = *reinterpret_cast<const uint4*>(xr[0] + k + i * 4 * EPC);
       if (two) {
-        const uint4 x1 = *reinterpret_cast<const uint4*>(xr[1] + k);
-        acc[1] = mfma16(w, x1, acc[1], T());
-        if (SWIGLU) accg[1] = mfma16(wg, x1, accg[1], T());
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x1[i] = *reinterpret_cast<const uint4*>(xr[1] + k + i * 4 * EPC);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[0] = mfma16(w[i], x0[i], acc[0], T());
+        if (SWIGLU) acc[2] = mfma16(wg[i], x0[i], acc[2], T());
+        if (two) {
+          acc[1] = mfma16(w[i], x1[i], acc[1], T());
+          if (SWIGLU) acc[3] = mfma16(wg[i], x1[i], acc[3], T());
+        }
       }
     }
-    // lane holds columns n0 + 4*fg + t of row t0 + j*16 + fr
+    // add the K slices in slice order
+    if (ks > 0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rl = t0 + j * 16 + fr;
-      if (rl >= cnt) continue;
-      const int64_t orow = beg + rl;
-      const int n = n0 + 4 * fg;
-      if (KIND == GEMM_UP) {
-        float h[4];
+      for (int j = 0; j < NACC; ++j) s_red[ks - 1][cg][j][lane] = acc[j];
+    }
+    __syncthreads();
+    if (ks == 0) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float u = acc[j][t];
-          if (SWIGLU) h[t] = silu(accg[j][t]) * u;
-          else if (ACT == ACT_GELU_TANH) h[t] = gelu_tanh(u);
-          else h[t] = gelu_erf(u);
+      for (int q = 0; q < SL - 1; ++q)
+#pragma unroll
+        for (int j = 0; j < NACC; ++j) {
+          const floatx4_t o = s_red[q][cg][j][lane];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[j][t] += o[t];
         }
-        T* c = (T*)P.C + orow * P.ldc + n;
-        if (sizeof(T) == 2) {
-          uint2 v;
-          v.x = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-          v.y = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
-          *reinterpret_cast<uint2*>(c) = v;
+      // lane holds columns n0 + 4*fg + t of row t0 + j*16 + fr
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rl = t0 + j * 16 + fr;
+        if (rl >= cnt) continue;
+        const int64_t orow = beg + rl;
+        const int n = n0 + 4 * fg;
+        if (KIND == GEMM_UP) {
+          float h[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float u = acc[j][t];
+            if (SWIGLU) h[t] = silu(acc[2 + j][t]) * u;
+            else if (ACT == ACT_GELU_TANH) h[t] = gelu_tanh(u);
+            else h[t] = gelu_erf(u);
+          }
+          T* c = (T*)P.C + orow * P.ldc + n;
+          if (sizeof(T) == 2) {
+            uint2 v;
+            v.x = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
+            v.y = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+            *reinterpret_cast<uint2*>(c) = v;
+          } else {
+            *reinterpret_cast<float4*>(c) = make_float4(h[0], h[1], h[2], h[3]);
+          }
         } else {
-          *reinterpret_cast<float4*>(c) = make_float4(h[0], h[1], h[2], h[3]);
+          float* c = (float*)P.C + orow * P.ldc + n;
+          *reinterpret_cast<float4*>(c) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
         }
-      } else {
-        float* c = (float*)P.C + orow * P.ldc + n;
-        *reinterpret_cast<float4*>(c) = make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
       }
     }
+    __syncthreads();   // s_red is reused by the next pass
   }
 }
 
 bool stream_gemm_supported(int dtype, int kind, int act, int N, int K) {
-  const int step = dtype == 0 ? 32 : 16;
+  const int step = dtype == 0 ? 128 : 64;   // K elements per block
   (void)kind;
   (void)act;
   return N > 0 && N % 64 == 0 && K > 0 && K % step == 0;
 }
 
+template <typename T, int KIND, int ACT, int G, int SL>
+static void stream_shape(const GemmProblem& la, int max_active, hipStream_t st) {
+  const dim3 grid(la.N / (16 * G), max_active);
+  auto kfn = k_stream_gemm<T, KIND, ACT, G, SL>;
+  MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 64 * G * SL, 0, st, la);
+}
+
+// Shape: 16 waves per workgroup by default (4 column groups x 4 K slices). When that gives fewer
+// workgroups than compute units, 2 x 8 (twice the workgroups); when each K slice would get fewer
+// than 4 blocks of K, 4 x 2.
 template <typename T, int KIND, int ACT>
-static void stream_t(const GemmProblem& la, dim3 grid, hipStream_t st) {
-  auto kfn = k_stream_gemm<T, KIND, ACT>;
-  MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+static void stream_t(const GemmProblem& la, int max_active, hipStream_t st) {
+  constexpr int KB = 16 * Elem<T>::kPer16B;
+  const int nblk = la.K / KB;
+  if ((la.N / 64) * max_active < 256) stream_shape<T, KIND, ACT, 2, 8>(la, max_active, st);
+  else if (nblk < 16) stream_shape<T, KIND, ACT, 4, 2>(la, max_active, st);
+  else stream_shape<T, KIND, ACT, 4, 4>(la, max_active, st);
 }
 
 template <typename T>
-static void launch_stream_t(const GemmProblem& la, int kind, int act, dim3 grid, hipStream_t st) {
-  if (kind == GEMM_DOWN) stream_t<T, GEMM_DOWN, ACT_GELU>(la, grid, st);
-  else if (act == ACT_SWIGLU) stream_t<T, GEMM_UP, ACT_SWIGLU>(la, grid, st);
-  else if (act == ACT_GELU_TANH) stream_t<T, GEMM_UP, ACT_GELU_TANH>(la, grid, st);
-  else stream_t<T, GEMM_UP, ACT_GELU>(la, grid, st);
+static void launch_stream_t(const GemmProblem& la, int kind, int act, int max_active, hipStream_t st) {
+  if (kind == GEMM_DOWN) stream_t<T, GEMM_DOWN, ACT_GELU>(la, max_active, st);
+  else if (act == ACT_SWIGLU) stream_t<T, GEMM_UP, ACT_SWIGLU>(la, max_active, st);
+  else if (act == ACT_GELU_TANH) stream_t<T, GEMM_UP, ACT_GELU_TANH>(la, max_active, st);
+  else stream_t<T, GEMM_UP, ACT_GELU>(la, max_active, st);
 }
 
 hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, hipStream_t st) {
   if (max_active <= 0 || !p.offsets) return hipSuccess;
-  dim3 grid(p.N / 64, max_active);
-  if (dtype == 0) launch_stream_t<bf16_t>(p, kind, act, grid, st);
-  else launch_stream_t<float>(p, kind, act, grid, st);
+  if (dtype == 0) launch_stream_t<bf16_t>(p, kind, act, max_active, st);
+  else launch_stream_t<float>(p, kind, act, max_active, st);
   return hipGetLastError();
 }
 

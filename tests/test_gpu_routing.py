@@ -18,8 +18,8 @@ def _spec(**kw):
     return LayerSpec(**base)
 
 
-def _route(spec, keys32, input_probs=False):
-    flags = moe.MOE_F_INPUT_PROBS if input_probs else 0
+def _route(spec, keys32, input_probs=False, multi=False):
+    flags = (moe.MOE_F_INPUT_PROBS if input_probs else 0) | (moe.MOE_F_ROUTE_MULTI if multi else 0)
     desc = moe.desc_from_spec(spec, flags)
     rb = moe.alloc_routing(desc)
     ws = moe.workspace(desc)
@@ -65,14 +65,16 @@ TC_CASES = [
 ]
 
 
+# multi=False lets small calls take the one-workgroup kernel; multi=True forces the multi-launch path
+@pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("case", TC_CASES)
-def test_tc_route_bitexact_on_logits(case):
+def test_tc_route_bitexact_on_logits(case, multi):
     S, Eh, ni, nz, nc, k = case
     spec = _spec(S=S, E_heavy=Eh, n_identity=ni, n_zero=nz, n_const=nc, k=k)
-    say(f"tc route logits S={S} E_r={spec.E_routed} k={k}")
+    say(f"tc route logits S={S} E_r={spec.E_routed} k={k} multi={multi}")
     rng = np.random.default_rng(S + Eh)
     L = _logits(rng, S, spec.E_routed)
-    got, _ = _route(spec, L)
+    got, _ = _route(spec, L, multi=multi)
     L64 = L.astype(np.float64)
     idx = orc.tc_select(L64, k)
     assert np.array_equal(got["topk_idx"], idx)
@@ -82,14 +84,14 @@ def test_tc_route_bitexact_on_logits(case):
     _check_permutation(spec, got, idx)
 
 
-@pytest.mark.parametrize("renorm", [True, False])
-def test_tc_route_bitexact_on_probs_with_reuse(renorm):
-    S, E = 3000, 8
+@pytest.mark.parametrize("renorm,S", [(True, 3000), (False, 3000), (True, 1500)])
+def test_tc_route_bitexact_on_probs_with_reuse(renorm, S):
+    E = 8
     spec = _spec(S=S, E_heavy=E, k=2, renorm=renorm, reuse_tau=0.3)
     rng = np.random.default_rng(7)
     L = _logits(rng, S, E, scale=1.2, tie_rows=0.1).astype(np.float64)
     P32 = orc.softmax(L).astype(np.float32)
-    say(f"tc route probs renorm={renorm}")
+    say(f"tc route probs renorm={renorm} S={S}")
     got, _ = _route(spec, P32, input_probs=True)
     P = P32.astype(np.float64)
     idx = orc.tc_select(P, 2)
@@ -154,15 +156,16 @@ DES_CASES = [
 ]
 
 
+@pytest.mark.parametrize("multi", [False, True])
 @pytest.mark.parametrize("case", DES_CASES)
-def test_des_route_bitexact_on_probs(case):
+def test_des_route_bitexact_on_probs(case, multi):
     N, E, K, M, k = case
     spec = _spec(S=N, E_heavy=E, mode="des", k=k, vote_k=K, m_core=M)
     rng = np.random.default_rng(N * E)
     L = _logits(rng, N, E, scale=0.9, tie_rows=0.2).astype(np.float64)
     P32 = orc.softmax(L).astype(np.float32)
-    say(f"des route N={N} E={E} K={K} M={M} k={k}")
-    got, _ = _route(spec, P32, input_probs=True)
+    say(f"des route N={N} E={E} K={K} M={M} k={k} multi={multi}")
+    got, _ = _route(spec, P32, input_probs=True, multi=multi)
     P = P32.astype(np.float64)
     votes, core = orc.des_vote(P, P, K, M, vote_dtype=np.float32)
     assert np.array_equal(got["votes"], votes)
