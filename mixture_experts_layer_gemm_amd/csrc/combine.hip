@@ -69,8 +69,10 @@ hipError_t launch_gather(int dtype, const void* x, const int32_t* row_token, con
   return hipGetLastError();
 }
 
-template <typename T, bool EC>
+// KM: an upper bound on k (2, 4, 8 or 16), which sizes the per-slot registers
+template <typename T, bool EC, int KM>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr int GRP = KM < 4 ? KM : 4;   // slots whose rows are loaded together
   const int cpr = a.d >> 3;
   const size_t total = (size_t)a.S * cpr;
   const T* x = (const T*)a.x;
@@ -83,23 +85,49 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
     if (reused) {
       load8<T>((const T*)a.cache + (size_t)s * a.d + c0, routed);
     } else if (!EC) {
-      for (int j = 0; j < a.k; ++j) {
-        const int e = a.topk_idx[(size_t)s * a.k + j];
-        const float w = a.topk_w[(size_t)s * a.k + j];
-        int l = e - a.E_heavy;
-        if (l < 0) {
-          const int r = a.token_rows[(size_t)s * a.k + j];
-          load8<float>(a.y_perm + (size_t)r * a.d + c0, v);
-        } else if (l < a.n_identity) {
-          load8<T>(x + (size_t)s * a.d + c0, v);
-        } else if ((l -= a.n_identity) < a.n_zero) {
-          continue;
-        } else {
-          l -= a.n_zero;
-          load8<T>((const T*)a.const_vec + (size_t)l * a.d + c0, v);
-        }
+      // the slots' metadata first, then their rows GRP at a time, added in slot order: the loads of
+      // a group are in flight together instead of one dependent pair per slot
+      int src_kind[KM], src_row[KM];
+      float src_w[KM];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) routed[q] += w * v[q];
+      for (int j = 0; j < KM; ++j) {
+        src_kind[j] = 0;   // 0: nothing, 1: routed row, 2: x, 3: constant row
+        src_row[j] = 0;
+        src_w[j] = 0.f;
+        if (j < a.k) {
+          const int e = a.topk_idx[(size_t)s * a.k + j];
+          src_w[j] = a.topk_w[(size_t)s * a.k + j];
+          int l = e - a.E_heavy;
+          if (l < 0) {
+            src_kind[j] = 1;
+            src_row[j] = a.token_rows[(size_t)s * a.k + j];
+          } else if (l < a.n_identity) {
+            src_kind[j] = 2;
+          } else if ((l -= a.n_identity) >= a.n_zero) {
+            src_kind[j] = 3;
+            src_row[j] = l - a.n_zero;
+          }
+        }
+      }
+#pragma unroll
+      for (int j0 = 0; j0 < KM; j0 += GRP) {
+        if (j0 < a.k) {
+          float vv[GRP][8];
+#pragma unroll
+          for (int jj = 0; jj < GRP; ++jj) {
+            const int j = j0 + jj;
+            if (src_kind[j] == 1) load8<float>(a.y_perm + (size_t)src_row[j] * a.d + c0, vv[jj]);
+            else if (src_kind[j] == 2) load8<T>(x + (size_t)s * a.d + c0, vv[jj]);
+            else if (src_kind[j] == 3) load8<T>((const T*)a.const_vec + (size_t)src_row[j] * a.d + c0, vv[jj]);
+          }
+#pragma unroll
+          for (int jj = 0; jj < GRP; ++jj) {
+            if (src_kind[j0 + jj] != 0) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) routed[q] += src_w[j0 + jj] * vv[jj][q];
+            }
+          }
+        }
       }
     } else {
       const int q0 = a.token_off[s], q1 = a.token_off[s + 1];
@@ -132,8 +160,22 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
 
 template <typename T, bool EC>
 static void combine_t(const CombineArgs& a, int blocks, hipStream_t st) {
-  auto kfn = k_combine<T, EC>;
-  MOE_LAUNCH("combine", kfn, blocks, 256, 0, st, a);
+  if (EC || a.k <= 2) {   // expert choice reads its rows through the token CSR: no slot registers
+    auto kfn = k_combine<T, EC, 2>;
+    MOE_LAUNCH("combine", kfn, blocks, 256, 0, st, a);
+    return;
+  }
+  if constexpr (EC) return;
+  if (a.k <= 4) {
+    auto kfn = k_combine<T, EC, 4>;
+    MOE_LAUNCH("combine", kfn, blocks, 256, 0, st, a);
+  } else if (a.k <= 8) {
+    auto kfn = k_combine<T, EC, 8>;
+    MOE_LAUNCH("combine", kfn, blocks, 256, 0, st, a);
+  } else {
+    auto kfn = k_combine<T, EC, 16>;
+    MOE_LAUNCH("combine", kfn, blocks, 256, 0, st, a);
+  }
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t st) {

@@ -12,11 +12,16 @@
 // Selection order everywhere: key descending, expert index ascending on ties. Keys are the fp32
 // logits (or given probabilities), compared exactly.
 #include <float.h>
+#include <limits.h>
 
 #include <algorithm>
 
 #include "common.hpp"
 #include "internal.hpp"
+
+// Wave-wide reductions of the device library (DPP based; every lane of the wave must be active).
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_max_f32(float);
+extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
 
 namespace moe {
 
@@ -120,12 +125,14 @@ hipError_t launch_router(int dtype, const void* x, const void* w_router, const f
 // lane holding V = ceil(E/LPT) of them (expert e lives in lane e % LPT, slot e / LPT).
 template <int LPT>
 __device__ __forceinline__ float group_max(float v) {
+  if constexpr (LPT == 64) return __ockl_wfred_max_f32(v);   // whole wave: DPP reduction
 #pragma unroll
   for (int o = LPT / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 template <int LPT>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (LPT == 64) return __ockl_wfred_add_f32(v);   // whole wave: DPP reduction
 #pragma unroll
   for (int o = LPT / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -497,12 +504,11 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
 
 // =============================================================================================
 // Small calls (a DES decode block, a tiny batch): the whole routing of token choice or DES-Vote and
-// the counting-sort dispatch in one workgroup: one launch instead of four. Selections here are
-// computed by rank, one thread per (token, expert): rank(e) = the number of allowed experts o of the
-// token with key_o > key_e, or key_o == key_e and o < e; e is taken when rank(e) < k, into slot
-// rank(e). This is the same set and slot order as the iterative selection of k_route_topk /
-// k_route_des; votes are summed in the same order, and rows come out in the same (expert, token,
-// slot) order as the three permute kernels.
+// the counting-sort dispatch in one workgroup: one launch instead of four. The selections are the
+// same as in k_route_topk / k_route_des (the same keys, order and tie rule; for a token spread over
+// a whole wave, wave_topk takes each maximum with a DPP reduction instead of shuffles); votes are
+// summed in the same order, and rows come out in the same (expert, token, slot) order as the three
+// permute kernels. Barriers here wait for LDS only (lds_barrier).
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallMaxSE = 8192;     // S * E_r: keys and probabilities kept in LDS
@@ -514,13 +520,70 @@ bool route_small_supported(int S, int E_r, int k) {
          E_r <= 256 && k <= kMaxK;
 }
 
+// Barrier for LDS data only: waits for this wave's LDS operations but not for its global stores,
+// which a full __syncthreads would also wait for (their results are not read back here).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Integer with the order of the float (finite values).
+__device__ __forceinline__ int float_order(float f) {
+  const int b = __float_as_int(f);
+  return b >= 0 ? b : b ^ 0x7fffffff;
+}
+
+// Top-k of one token whose experts span the whole wave (expert e in lane e % 64, slot e / 64),
+// among experts allowed by `allow` (bit v of the lane's mask): k rounds of a wave-wide maximum
+// (a DPP reduction) and a ballot for the lowest expert index holding it. Same result as
+// token_topk<64, V>. Returns the lane's chosen-set bits; when out_e is given, the lane holding
+// the j-th chosen expert writes it and its probability to out_e[j], out_p[j] (key order).
+template <int V>
+__device__ __forceinline__ unsigned wave_topk(const float (&key)[V], const float (&p)[V], unsigned allow, int E,
+                                              int lane, int k, int* out_e, float* out_p) {
+  unsigned taken = 0;
+  int ord[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    ord[v] = float_order(key[v]);
+    if (!(lane + v * 64 < E && ((allow >> v) & 1u))) taken |= 1u << v;   // never eligible
+  }
+  for (int j = 0; j < k; ++j) {
+    int best = INT_MIN;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (!((taken >> v) & 1u)) best = max(best, ord[v]);
+    const int m = __ockl_wfred_max_i32(best);
+    bool done = false;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if (!done) {
+        const uint64_t hit = __ballot(!((taken >> v) & 1u) && ord[v] == m);
+        if (hit) {
+          done = true;
+          const int l = __ffsll((unsigned long long)hit) - 1;
+          if (lane == l) {
+            taken |= 1u << v;
+            if (out_e) {
+              out_e[j] = v * 64 + l;
+              out_p[j] = p[v];
+            }
+          }
+        }
+      }
+    }
+  }
+  // clear the never-eligible marks
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (!(lane + v * 64 < E && ((allow >> v) & 1u))) taken &= ~(1u << v);
+  return taken;
+}
+
 template <int LPT, int V, bool DES>
 __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, PermuteArgs q) {
   __shared__ float s_key[kSmallMaxSE];
   __shared__ float s_p[kSmallMaxSE];
-  __shared__ uint8_t s_taken[DES ? kSmallMaxSE : 1];
+  __shared__ float s_aux[DES ? kSmallMaxSE : 1];   // DES: filtered probabilities
   __shared__ float s_votes[256];
-  __shared__ int s_incore[256];
+  __shared__ int s_rank[256], s_core[256];
   __shared__ int s_idx[kSmallMaxPairs];
   __shared__ float s_w[kSmallMaxPairs];
   __shared__ uint8_t s_reuse[kSmallMaxS];
@@ -528,17 +591,21 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
   __shared__ int s_cnt[256], s_off[257], s_run[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, E = a.E_r, SE = S * E;
-  const int kk = DES ? min(a.k, a.m_core) : a.k;
+  const int M = a.m_core;
+  const int kk = DES ? min(a.k, M) : a.k;
 
   for (int i = tid; i < SE; i += kSmallThreads) s_key[i] = a.keys[i];
   for (int e = tid; e < 256; e += kSmallThreads) {
     s_cnt[e] = 0;
     s_run[e] = 0;
+    s_rank[e] = 0;
   }
   for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) (&s_wcnt[0][0])[i] = 0;
-  __syncthreads();
+  lds_barrier();
 
-  // probabilities: LPT lanes per token (max-subtracted softmax, or the given probabilities)
+  // probabilities: LPT lanes per token (max-subtracted softmax, or the given probabilities); then,
+  // DES: the filter (the top-vote_k experts of each token keep their probability); token choice:
+  // the top-kk selection
   constexpr int tpb = kSmallThreads / LPT;
   const int sub = lane & (LPT - 1);
   for (int base = 0; base < S; base += tpb) {
@@ -550,84 +617,108 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
 #pragma unroll
     for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
     pm = group_max<LPT>(pm);
+    int sel_e[kMaxK];
+    float sel_p[kMaxK];
+    const int kq = DES ? a.vote_k : kk;   // DES: the filter; token choice: the selection
+    unsigned taken;
+    if constexpr (LPT == 64)
+      taken = wave_topk<V>(key, p, ~0u, E, lane, kq, (DES || !live) ? nullptr : s_idx + s * kk, s_w + s * kk);
+    else
+      taken = token_topk<LPT, V>(key, p, ~0u, E, sub, lane, kq, DES ? nullptr : sel_e, sel_p);
     if (live) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int e = sub + v * LPT;
-        if (e < E) s_p[s * E + e] = p[v];
+        if (e < E) {
+          s_p[s * E + e] = p[v];
+          if constexpr (DES) s_aux[s * E + e] = ((taken >> v) & 1u) ? p[v] : 0.f;
+        }
       }
-      if (sub == 0) s_reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
+      if (sub == 0) {
+        s_reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
+        if constexpr (!DES && LPT < 64) {
+          for (int j = 0; j < kk; ++j) {
+            s_idx[s * kk + j] = sel_e[j];
+            s_w[s * kk + j] = sel_p[j];
+          }
+        }
+      }
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (a.probs)
     for (int i = tid; i < SE; i += kSmallThreads) a.probs[i] = s_p[i];
   if (a.reuse)
     for (int s = tid; s < S; s += kSmallThreads) a.reuse[s] = s_reuse[s];
 
-  // rank of (s, e) among the experts of s allowed by `ok`
-  auto rank_of = [&](int s, int e, auto ok) -> int {
-    const float* kr = s_key + s * E;
-    const float ke = kr[e];
-    int r = 0;
-#pragma unroll 8
-    for (int o = 0; o < E; ++o) {
-      const float ko = kr[o];
-      r += (ok(o) && (ko > ke || (ko == ke && o < e))) ? 1 : 0;
-    }
-    return r;
-  };
-
   if constexpr (DES) {
-    // filter: the top-vote_k experts of each token keep their probability
-    for (int i = tid; i < SE; i += kSmallThreads) {
-      const int s = i / E, e = i - s * E;
-      s_taken[i] = rank_of(s, e, [](int) { return true; }) < a.vote_k ? 1 : 0;
-    }
-    __syncthreads();
     // votes, summed over tokens in ascending order
     for (int e = tid; e < E; e += kSmallThreads) {
       float v = 0.f;
 #pragma unroll 8
-      for (int n = 0; n < S; ++n) v += s_taken[n * E + e] ? s_p[n * E + e] : 0.f;
+      for (int n = 0; n < S; ++n) v += s_aux[n * E + e];
       s_votes[e] = v;
       a.votes[e] = v;
     }
-    __syncthreads();
-    // elect: rank under (vote desc, index asc)
-    for (int e = tid; e < E; e += kSmallThreads) {
+    lds_barrier();
+    // elect: rank of e under (vote desc, index asc), one wave-wide ballot per (e, 64 rivals)
+    for (int t = wave; t < E * ((E + 63) / 64); t += kSmallWaves) {
+      const int e = t % E, o = (t / E) * 64 + lane;
       const float ve = s_votes[e];
-      int rank = 0;
-#pragma unroll 8
-      for (int o = 0; o < E; ++o) {
+      bool before = false;
+      if (o < E) {
         const float vo = s_votes[o];
-        rank += (vo > ve || (vo == ve && o < e)) ? 1 : 0;
+        before = vo > ve || (vo == ve && o < e);
       }
-      s_incore[e] = rank < a.m_core ? 1 : 0;
+      const int c = __popcll(__ballot(before));
+      if (lane == 0) atomicAdd(&s_rank[e], c);
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kSmallThreads) {
-      if (s_incore[e]) {
-        int pos = 0;
-#pragma unroll 8
-        for (int o = 0; o < e; ++o) pos += s_incore[o];
-        a.core[pos] = e;
+    lds_barrier();
+    // core = experts of rank < M, listed ascending
+    if (wave == 0) {
+      int cbase = 0;
+      for (int e0 = 0; e0 < E; e0 += 64) {
+        const int e = e0 + lane;
+        const bool in = e < E && s_rank[e] < M;
+        const uint64_t m = __ballot(in);
+        if (in) {
+          const int pos = cbase + __popcll(m & lanemask_lt());
+          s_core[pos] = e;
+          a.core[pos] = e;
+        }
+        cbase += __popcll(m);
       }
     }
-  }
-
-  // selection: slot rank(e) of token s holds e when rank(e) < kk (inside the core for DES)
-  for (int i = tid; i < SE; i += kSmallThreads) {
-    const int s = i / E, e = i - s * E;
-    if (DES && !s_incore[e]) continue;
-    const int r = DES ? rank_of(s, e, [&](int o) { return s_incore[o] != 0; })
-                      : rank_of(s, e, [](int) { return true; });
-    if (r < kk) {
-      s_idx[s * kk + r] = e;
-      s_w[s * kk + r] = s_p[i];
+    lds_barrier();
+    // selection: top-kk inside the core
+    for (int base = 0; base < S; base += tpb) {
+      const int s = base + tid / LPT;
+      const bool live = s < S;
+      float key[V], p[V];
+      unsigned allow = 0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = sub + v * LPT;
+        key[v] = (live && e < E) ? s_key[min(s, S - 1) * E + e] : -FLT_MAX;
+        p[v] = (live && e < E) ? s_p[min(s, S - 1) * E + e] : 0.f;
+        if (e < E && s_rank[e] < M) allow |= 1u << v;
+      }
+      if constexpr (LPT == 64) {
+        wave_topk<V>(key, p, allow, E, lane, kk, live ? s_idx + s * kk : nullptr, s_w + s * kk);
+      } else {
+        int sel_e[kMaxK];
+        float sel_p[kMaxK];
+        token_topk<LPT, V>(key, p, allow, E, sub, lane, kk, sel_e, sel_p);
+        if (live && sub == 0) {
+          for (int j = 0; j < kk; ++j) {
+            s_idx[s * kk + j] = sel_e[j];
+            s_w[s * kk + j] = sel_p[j];
+          }
+        }
+      }
     }
+    lds_barrier();
   }
-  __syncthreads();
   // weights: p, or p over the sum of the chosen p in slot order
   for (int s = tid; s < S; s += kSmallThreads) {
     float denom = 1.f;
@@ -645,7 +736,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       a.topk_w[(size_t)s * kk + j] = wj;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
   // dispatch: pair p = s * kk + j goes to a row when its expert is heavy and s does not reuse
   const int P = S * kk;
@@ -662,19 +753,35 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     int e;
     if (live_pair(p, e)) atomicAdd(&s_cnt[e], 1);
   }
-  __syncthreads();
-  for (int e = tid; e <= E; e += kSmallThreads) {
-    int off = 0;
-#pragma unroll 8
-    for (int o = 0; o < e; ++o) off += o < q.E_heavy ? s_cnt[o] : 0;
-    s_off[e] = off;
-    q.offsets[e] = off;
-    if (e < E) q.counts[e] = e < q.E_heavy ? s_cnt[e] : 0;
-    if (e == E) *q.n_rows = off;
+  lds_barrier();
+  // offsets: exclusive scan of the counts over experts (light experts count 0), one wave
+  if (wave == 0) {
+    int base = 0;
+    for (int e0 = 0; e0 < E; e0 += 64) {
+      const int e = e0 + lane;
+      const int c = (e < E && e < q.E_heavy) ? s_cnt[e] : 0;
+      int incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      if (e < E) {
+        s_off[e] = base + incl - c;
+        q.offsets[e] = base + incl - c;
+        q.counts[e] = c;
+      }
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) {
+      s_off[E] = base;
+      q.offsets[E] = base;
+      *q.n_rows = base;
+    }
   }
   int nbits = 1;
   while ((1 << nbits) <= q.E_heavy) ++nbits;
-  __syncthreads();
+  lds_barrier();
   for (int r0 = 0; r0 < P; r0 += kSmallThreads) {
     const int p = r0 + tid;
     int e;
@@ -688,7 +795,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     }
     const uint64_t lower = peers & lanemask_lt();
     if (ok && lower == 0) s_wcnt[wave][e] = __popcll(peers);
-    __syncthreads();
+    lds_barrier();
     if (ok) {
       int base = s_off[e] + s_run[e];
       for (int o = 0; o < wave; ++o) base += s_wcnt[o][e];
@@ -699,7 +806,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     } else if (p < P) {
       q.token_rows[p] = -1;
     }
-    __syncthreads();
+    lds_barrier();
     for (int i = tid; i < q.E_heavy; i += kSmallThreads) {
       int add = 0;
       for (int o = 0; o < kSmallWaves; ++o) {
@@ -708,7 +815,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       }
       s_run[i] += add;
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
