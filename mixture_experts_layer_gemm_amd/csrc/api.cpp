@@ -61,7 +61,7 @@ struct Plan {
   bool streaming = false;     // heavy experts on the weight-streaming kernel
   size_t esz = 0;             // element size of dtype
   // workspace pieces (byte offsets)
-  size_t o_blk = 0, o_filt = 0, o_pT = 0, o_mask = 0, o_tokrows = 0;   // route scratch
+  size_t o_blk = 0, o_filt = 0, o_pT = 0, o_tokrows = 0, o_tokcnt = 0;   // route scratch
   size_t o_logits = 0;                                                  // router output
   size_t o_rt = 0;                                                      // internal routing arrays
   size_t o_h = 0, o_hs = 0, o_yp = 0, o_ys = 0;                         // expert buffers
@@ -158,8 +158,8 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
   p->o_blk = take((size_t)nblk * std::max(d->E_heavy, 1) * 4);
   p->o_filt = take(d->mode == MOE_DES_VOTE ? S * Er * 4 : 0);
   p->o_pT = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
-  p->o_mask = take(d->mode == MOE_EXPERT_CHOICE ? S * ((Er + 31) / 32) * 4 : 0);
   p->o_tokrows = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
+  p->o_tokcnt = take(d->mode == MOE_EXPERT_CHOICE ? S * 4 : 0);
   p->o_logits = take(S * Er * 4);
   // internal routing arrays
   size_t r = 0;
@@ -261,8 +261,8 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
     a.keys = keys;
     a.probs = r->probs;
     a.pT = (float*)(w + p.o_pT);
-    a.tok_mask = (uint32_t*)(w + p.o_mask);
     a.tok_rows_tmp = (int32_t*)(w + p.o_tokrows);
+    a.tok_cnt = (int32_t*)(w + p.o_tokcnt);
     a.counts = r->counts;
     a.offsets = r->offsets;
     a.row_token = r->row_token;

@@ -5,10 +5,14 @@
 // construction and lets a token receive a variable number of experts; 容量因子: the capacity is
 // f_c * S / E (rounded down here, clipped to S).
 //
-// Kernels: (1) per token, the probabilities, stored expert-major pT[E][S]; (2) one workgroup per
-// expert: exact radix select of the C-th largest key (the fp32 bit pattern orders non-negative
-// floats), then a stable compaction in token order (equal keys: lowest token first); (3) the
-// per-token row lists (CSR, ascending expert) for the combine.
+// Kernels: (1) per block of 64 tokens (4 lanes per token), the probabilities, staged through LDS so
+// that both the token-major output and the expert-major copy pT[E][S] are written with coalesced
+// stores; (2) one
+// workgroup per expert: exact radix select of the C-th largest key (the fp32 bit pattern orders
+// non-negative floats; histogram atomics aggregated per wave), then a stable compaction in token
+// order (equal keys: lowest token first) from one workgroup-wide scan; every token's row for the
+// expert (or -1) goes to rowsT[E][S] and the token's expert count is incremented; (3) the per-token
+// row lists (CSR, ascending expert) for the combine.
 #include <float.h>
 
 #include "common.hpp"
@@ -16,75 +20,154 @@
 
 namespace moe {
 
-constexpr int kECMaxE = 256;
+constexpr int kProbTok = 64;       // tokens per probability workgroup
 constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
 
-__global__ __launch_bounds__(256) void k_ec_probs(ECArgs a) {
-  const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= a.S) return;
-  const float* row = a.keys + (size_t)s * a.E;
-  if (a.input_probs) {
-    for (int e = 0; e < a.E; ++e) {
-      const float p = row[e];
-      a.pT[(size_t)e * a.S + s] = p;
-      if (a.probs) a.probs[(size_t)s * a.E + e] = p;
+constexpr int kProbLanes = 4;   // lanes per token (expert e handled by lane e % 4 of its group)
+
+__global__ __launch_bounds__(kProbTok * kProbLanes) void k_ec_probs(ECArgs a) {
+  __shared__ float s_blk[kProbTok * 257];   // [token][expert], row stride E + 1
+  constexpr int NT = kProbTok * kProbLanes;
+  const int E = a.E, ld = E + 1;
+  const int s0 = blockIdx.x * kProbTok;
+  const int ns = min(kProbTok, a.S - s0);
+  const float* kb = a.keys + (size_t)s0 * E;
+  for (int i = threadIdx.x; i < ns * E; i += NT) s_blk[(i / E) * ld + i % E] = kb[i];
+  __syncthreads();
+  const int t = threadIdx.x / kProbLanes, q = threadIdx.x % kProbLanes;
+  if (!a.input_probs) {   // uniform: all lanes of a group take part in the shuffles
+    float* row = s_blk + min(t, ns - 1) * ld;
+    float m = -FLT_MAX;
+    for (int e = q; e < E; e += kProbLanes) m = fmaxf(m, row[e]);
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 2, 64));
+    float z = 0.f;
+    for (int e = q; e < E; e += kProbLanes) z += expf(row[e] - m);
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    const float inv = 1.0f / z;
+    __syncthreads();
+    if (t < ns)
+      for (int e = q; e < E; e += kProbLanes) row[e] = expf(row[e] - m) * inv;
+    __syncthreads();
+  }
+  if (a.probs) {
+    float* pb = a.probs + (size_t)s0 * E;
+    for (int i = threadIdx.x; i < ns * E; i += NT) pb[i] = s_blk[(i / E) * ld + i % E];
+  }
+  for (int i = threadIdx.x; i < E * kProbTok; i += NT) {
+    const int e = i / kProbTok, tt = i % kProbTok;
+    if (tt < ns) a.pT[(size_t)e * a.S + s0 + tt] = s_blk[tt * ld + e];
+  }
+  if ((int)threadIdx.x < ns) a.tok_cnt[s0 + threadIdx.x] = 0;   // experts per token, counted by k_ec_select
+}
+
+// Exclusive prefix over the workgroup (threads in order) of two counts, and their totals.
+__device__ __forceinline__ void block_scan2(int x, int y, int* s_w, int& xb, int& yb, int& xt, int& yt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int vx = x, vy = y;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tx = __shfl_up(vx, o, 64), ty = __shfl_up(vy, o, 64);
+    if (lane >= o) {
+      vx += tx;
+      vy += ty;
     }
-    return;
   }
-  float m = -FLT_MAX;
-  for (int e = 0; e < a.E; ++e) m = fmaxf(m, row[e]);
-  float z = 0.f;
-  for (int e = 0; e < a.E; ++e) z += expf(row[e] - m);
-  const float inv = 1.0f / z;
-  for (int e = 0; e < a.E; ++e) {
-    const float p = expf(row[e] - m) * inv;
-    a.pT[(size_t)e * a.S + s] = p;
-    if (a.probs) a.probs[(size_t)s * a.E + e] = p;
-  }
-}
-
-// Exclusive prefix of a 0/1 flag over the workgroup (threads in order), and the total.
-__device__ __forceinline__ int block_flag_scan(bool f, int* s_w, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const uint64_t m = __ballot(f);
-  const int in_wave = __popcll(m & lanemask_lt());
-  if (lane == 0) s_w[wave] = __popcll(m);
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int c = s_w[w];
-    before += (w < wave) ? c : 0;
-    tot += c;
+  if (lane == 63) {
+    s_w[2 * wave] = vx;
+    s_w[2 * wave + 1] = vy;
   }
   __syncthreads();
-  total = tot;
-  return before + in_wave;
+  int bx = 0, by = 0, tx = 0, ty = 0;
+  for (int w = 0; w < kSelWaves; ++w) {
+    const int cx = s_w[2 * w], cy = s_w[2 * w + 1];
+    if (w < wave) {
+      bx += cx;
+      by += cy;
+    }
+    tx += cx;
+    ty += cy;
+  }
+  __syncthreads();
+  xb = bx + vx - x;
+  yb = by + vy - y;
+  xt = tx;
+  yt = ty;
 }
 
+// Thread t owns the tokens [t * per, (t + 1) * per), per = ceil(S / kSelThreads). With REG, per <=
+// kSelRegs and the keys stay in registers across the radix passes.
+constexpr int kSelRegs = 16;
+
+template <bool REG>
 __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
   __shared__ int hist[256];
   __shared__ int s_sel, s_rem;
-  __shared__ int s_w[kSelThreads / 64];
+  __shared__ int s_w[2 * kSelWaves];
   const int e = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(a.pT + (size_t)e * a.S);
+  const int per = (a.S + kSelThreads - 1) / kSelThreads;
+  const int s_beg = min(a.S, (int)threadIdx.x * per), s_end = min(a.S, s_beg + per);
+  uint32_t ureg[REG ? kSelRegs : 1];
+  if constexpr (REG) {
+#pragma unroll
+    for (int j = 0; j < kSelRegs; ++j) ureg[j] = (j < per && s_beg + j < s_end) ? keys[s_beg + j] : 0u;
+  }
+  auto key = [&](int j) -> uint32_t {
+    if constexpr (REG) return ureg[j];
+    else return keys[s_beg + j];
+  };
   uint32_t prefix = 0, pmask = 0;
   int remaining = a.C;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
     __syncthreads();
-    for (int s = threadIdx.x; s < a.S; s += kSelThreads) {
-      const uint32_t u = keys[s];
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+#pragma unroll
+    for (int j = 0; j < (REG ? kSelRegs : 1); ++j) {
+      for (int jj = REG ? j : 0; jj < (REG ? j + 1 : per); ++jj) {
+        if (REG && j >= per) break;
+        const bool valid = s_beg + jj < s_end;
+        const uint32_t u = valid ? key(jj) : 0u;
+        const bool in = valid && (u & pmask) == prefix;
+        const int bin = in ? (int)((u >> shift) & 255u) : 256;
+        // lanes with the same bin add once: match the 9-bit bin over the wave
+        uint64_t peers = ~0ull;
+#pragma unroll
+        for (int b = 0; b < 9; ++b) {
+          const bool bit = (bin >> b) & 1;
+          const uint64_t m = __ballot(bit);
+          peers &= bit ? m : ~m;
+        }
+        if (in && (peers & lanemask_lt()) == 0) atomicAdd(&hist[bin], __popcll(peers));
+      }
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      int cum = 0, sel = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= remaining) { sel = b; break; }
-        cum += hist[b];
+    // the bin holding the remaining-th largest key: wave 0 scans the bins from the top
+    if (threadIdx.x < 64) {
+      int v[4], run = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = hist[255 - 4 * lane - j];
+        run += v[j];
       }
-      s_sel = sel;
-      s_rem = remaining - cum;
+      int incl = run;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      int above = incl - run;   // keys in bins above this lane's first bin
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (above < remaining && above + v[j] >= remaining) {
+          s_sel = 255 - 4 * lane - j;
+          s_rem = remaining - above;
+        }
+        above += v[j];
+      }
     }
     __syncthreads();
     prefix |= (uint32_t)s_sel << shift;
@@ -93,99 +176,100 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
     __syncthreads();
   }
   const uint32_t T = prefix;      // the C-th largest key
-  const int need_eq = remaining;  // keys equal to T still to take (lowest tokens first)
-  const int mw = (a.E + 31) >> 5;
-  int eq_base = 0, take_base = 0;
-  for (int base = 0; base < a.S; base += kSelThreads) {
-    const int s = base + threadIdx.x;
-    const uint32_t u = s < a.S ? keys[s] : 0u;
-    const bool gt = s < a.S && u > T;
-    const bool eq = s < a.S && u == T;
-    int eq_tot, take_tot;
-    const int eq_rank = eq_base + block_flag_scan(eq, s_w, eq_tot);
-    const bool take = gt || (eq && eq_rank < need_eq);
-    const int pos = take_base + block_flag_scan(take, s_w, take_tot);
+  const int need_eq = remaining;  // keys equal to T to take, lowest tokens first
+  int n_gt = 0, n_eq = 0;
+  for (int j = 0; j < s_end - s_beg; ++j) {
+    const uint32_t u = key(j);
+    n_gt += u > T ? 1 : 0;
+    n_eq += u == T ? 1 : 0;
+  }
+  int gt_before, eq_before, gt_tot, eq_tot;
+  block_scan2(n_gt, n_eq, s_w, gt_before, eq_before, gt_tot, eq_tot);
+  int eq_rank = eq_before;
+  int pos = gt_before + min(eq_before, need_eq);
+  int32_t* rows_e = a.tok_rows_tmp + (size_t)e * a.S;
+  for (int j = 0; j < s_end - s_beg; ++j) {
+    const int s = s_beg + j;
+    const uint32_t u = key(j);
+    bool take = u > T;
+    if (u == T) take = eq_rank++ < need_eq;
+    int row = -1;
     if (take) {
-      const int row = e * a.C + pos;
+      row = e * a.C + pos++;
       a.row_token[row] = s;
       a.row_w[row] = __uint_as_float(u);
-      a.tok_rows_tmp[(size_t)s * a.E + e] = row;
-      atomicOr(&a.tok_mask[(size_t)s * mw + (e >> 5)], 1u << (e & 31));
+      atomicAdd(&a.tok_cnt[s], 1);
     }
-    eq_base += eq_tot;
-    take_base += take_tot;
+    rows_e[s] = row;
   }
 }
 
-// One workgroup: CSR offsets of every token's rows, plus the fixed per-expert counts/offsets.
-__global__ __launch_bounds__(kSelThreads) void k_ec_csr_scan(ECArgs a) {
-  __shared__ int s_w[kSelThreads / 64];
+// Every token's rows in ascending expert order (CSR), kCsrTok tokens per workgroup: the offset of
+// the workgroup's first token is the sum of the counts before it (read directly: S ints), then a
+// workgroup scan; the first workgroup also writes the fixed per-expert counts / offsets.
+constexpr int kCsrTok = 256;
+
+__global__ __launch_bounds__(kCsrTok) void k_ec_csr(ECArgs a) {
+  __shared__ int s_w[2 * (kCsrTok / 64)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int mw = (a.E + 31) >> 5;
-  int run = 0;
-  for (int base = 0; base < a.S; base += kSelThreads) {
-    const int s = base + threadIdx.x;
-    int c = 0;
-    if (s < a.S)
-      for (int w = 0; w < mw; ++w) c += __popc(a.tok_mask[(size_t)s * mw + w]);
-    // inclusive wave scan
-    int v = c;
+  const int s0 = blockIdx.x * kCsrTok;
+  int before = 0;
+  for (int i = threadIdx.x; i < s0; i += kCsrTok) before += a.tok_cnt[i];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(v, o, 64);
-      if (lane >= o) v += t;
+  for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+  const int s = s0 + threadIdx.x;
+  const int c = s < a.S ? a.tok_cnt[s] : 0;
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 0) s_w[wave] = before;
+  if (lane == 63) s_w[kCsrTok / 64 + wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < kCsrTok / 64; ++w) base += s_w[w];   // the prefix before s0, summed by all waves
+  for (int w = 0; w < wave; ++w) base += s_w[kCsrTok / 64 + w];
+  int pos = base + incl - c;
+  if (s < a.S) {
+    a.token_off[s] = pos;
+    for (int e0 = 0; e0 < a.E; e0 += 8) {   // eight loads in flight, then the writes in expert order
+      int r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r[j] = e0 + j < a.E ? a.tok_rows_tmp[(size_t)(e0 + j) * a.S + s] : -1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (r[j] >= 0) a.token_list[pos++] = r[j];
     }
-    if (lane == 63) s_w[wave] = v;
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-      before += (w < wave) ? s_w[w] : 0;
-      tot += s_w[w];
+    if (s == a.S - 1) a.token_off[a.S] = pos;
+  }
+  if (blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < a.E; e += kCsrTok) {
+      a.counts[e] = a.C;
+      a.offsets[e] = e * a.C;
     }
-    __syncthreads();
-    if (s < a.S) a.token_off[s] = run + before + v - c;
-    run += tot;
-  }
-  if (threadIdx.x == 0) a.token_off[a.S] = run;
-  for (int e = threadIdx.x; e < a.E; e += kSelThreads) {
-    a.counts[e] = a.C;
-    a.offsets[e] = e * a.C;
-  }
-  if (threadIdx.x == 0) {
-    a.offsets[a.E] = a.E * a.C;
-    *a.n_rows = a.E * a.C;
-    if (a.capacity) *a.capacity = a.C;
-  }
-}
-
-__global__ __launch_bounds__(256) void k_ec_csr_fill(ECArgs a) {
-  const int s = blockIdx.x * 256 + threadIdx.x;
-  if (s >= a.S) return;
-  const int mw = (a.E + 31) >> 5;
-  int pos = a.token_off[s];
-  for (int w = 0; w < mw; ++w) {
-    uint32_t m = a.tok_mask[(size_t)s * mw + w];
-    while (m) {
-      const int b = __ffs(m) - 1;
-      m &= m - 1;
-      const int e = w * 32 + b;
-      a.token_list[pos++] = a.tok_rows_tmp[(size_t)s * a.E + e];
+    if (threadIdx.x == 0) {
+      a.offsets[a.E] = a.E * a.C;
+      *a.n_rows = a.E * a.C;
+      if (a.capacity) *a.capacity = a.C;
     }
   }
 }
 
 hipError_t launch_route_ec(const ECArgs& a, hipStream_t st) {
-  const int mw = (a.E + 31) >> 5;
-  hipError_t err = launch_fill_u32(a.tok_mask, 0u, (size_t)a.S * mw, st);
-  if (err != hipSuccess) return err;
+  if (a.E > 256) return hipErrorInvalidValue;
   auto k1 = k_ec_probs;
-  MOE_LAUNCH("ec_probs", k1, (a.S + 255) / 256, 256, 0, st, a);
-  auto k2 = k_ec_select;
-  MOE_LAUNCH("ec_select", k2, a.E, kSelThreads, 0, st, a);
-  auto k3 = k_ec_csr_scan;
-  MOE_LAUNCH("ec_csr_scan", k3, 1, kSelThreads, 0, st, a);
-  auto k4 = k_ec_csr_fill;
-  MOE_LAUNCH("ec_csr_fill", k4, (a.S + 255) / 256, 256, 0, st, a);
+  MOE_LAUNCH("ec_probs", k1, (a.S + kProbTok - 1) / kProbTok, kProbTok * kProbLanes, 0, st, a);
+  if ((a.S + kSelThreads - 1) / kSelThreads <= kSelRegs) {
+    auto k2 = k_ec_select<true>;
+    MOE_LAUNCH("ec_select", k2, a.E, kSelThreads, 0, st, a);
+  } else {
+    auto k2 = k_ec_select<false>;
+    MOE_LAUNCH("ec_select", k2, a.E, kSelThreads, 0, st, a);
+  }
+  auto k3 = k_ec_csr;
+  MOE_LAUNCH("ec_csr", k3, (a.S + kCsrTok - 1) / kCsrTok, kCsrTok, 0, st, a);
   return hipGetLastError();
 }
 

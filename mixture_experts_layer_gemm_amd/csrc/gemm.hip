@@ -8,7 +8,7 @@
 // experts are extra problems in the same launch (all S rows; their down projections are one GEMM
 // over the K-concatenation of their hidden activations).
 //
-// Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 256}; each wave
+// Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 192, 256}; each wave
 // owns 128 rows x BN/2 weight rows, which keeps LDS reads at 2/3 of a 128 x 64 split):
 //   * K advances 128 bytes per stage (64 bf16 / 32 fp32); A and B stages are double-buffered in
 //     LDS (2 x (32 KB + BN*128 B)) and filled by direct global->LDS loads (no staging registers),
@@ -153,7 +153,7 @@ __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& 
 }
 
 // Placement of the work of one K step: NM MFMAs; NF LDS reads, read q right before MFMA
-// (q * NM) / NF; LPS global->LDS loads, load d right before MFMA (d * NM) / LPS. An "MFMA" here is
+// read_pos(q); LPS global->LDS loads, load d right before MFMA (d * NM) / LPS. An "MFMA" here is
 // one 16x16 product step, MPC instructions. region<M0, M1>() pins the order of the LDS reads and
 // MFMAs of MFMAs [M0, M1) (loads bound the regions).
 template <int NM, int NF, int LPS, int MPC>
@@ -164,10 +164,17 @@ struct step_sched {
       if (load_pos(d) == m) return d;
     return -1;
   }
-  static constexpr bool read_at(int m) {
-    const int q = (m * NF + NM - 1) / NM;
-    return q < NF && (q * NM) / NF == m;
+  // the reads are spread over the first 3/4 of the MFMAs, so that they have landed when the next
+  // step starts
+  static constexpr int RSPAN = NM - NM / 4;
+  static_assert(RSPAN >= NF, "one read per MFMA slot at most");
+  static constexpr int read_pos(int q) { return (q * RSPAN) / NF; }
+  static constexpr int read_at_q(int m) {
+    for (int q = 0; q < NF; ++q)
+      if (read_pos(q) == m) return q;
+    return -1;
   }
+  static constexpr bool read_at(int m) { return read_at_q(m) >= 0; }
   // MFMAs from m up to (not including) the next read position or m1
   static constexpr int run(int m, int m1) {
     int e = m + 1;
@@ -375,8 +382,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
         SS::template region<SS::load_pos(d - 1), m>();
         dma_one(dma, std::integral_constant<int, d>{});
       }
-      constexpr int q = (m * NF + NM - 1) / NM;   // the read that belongs right before MFMA m, if any
-      if constexpr (q < NF && (q * NM) / NF == m) nxt[q] = read_frag(next, std::integral_constant<int, q>{});
+      constexpr int q = SS::read_at_q(m);   // the read that belongs right before MFMA m, if any
+      if constexpr (q >= 0) nxt[q] = read_frag(next, std::integral_constant<int, q>{});
       constexpr int i = m / MJ, j = m % MJ;
       acc[i][j] = mfma16(cur[MJ + i], cur[j], acc[i][j], T());
       self(self, std::integral_constant<int, m + 1>{}, next, dma, cur, nxt);
@@ -457,11 +464,16 @@ static int out_cols_per_tile(int kind, int act, int BN) { return (kind == GEMM_U
 
 // The 256-row weight tile keeps LDS reads per MFMA lower than the 128-row one, so it is used
 // unless padding N up to whole tiles would waste more than 1/8 of the work.
+// Tile width: 256 unless that pads N by more than 1/8; then 192 if it pads less than 256 does,
+// else 128. (256 reads the fewest bytes per FLOP; 192 fits N = 4.5 x 256 exactly.)
 static int pick_bn(int kind, int act, int N) {
   if (N <= 0 || N % 64 != 0) return 0;
-  const int c256 = out_cols_per_tile(kind, act, 256);
-  const int64_t padded = ((int64_t)N + c256 - 1) / c256 * c256;
-  if (padded * 8 <= (int64_t)N * 9) return 256;
+  auto padded = [&](int bn) {
+    const int c = out_cols_per_tile(kind, act, bn);
+    return ((int64_t)N + c - 1) / c * c;
+  };
+  if (padded(256) * 8 <= (int64_t)N * 9) return 256;
+  if (padded(192) < padded(256) && padded(192) * 8 <= (int64_t)N * 9) return 192;
   return 128;
 }
 
@@ -479,6 +491,7 @@ static void launch_t(const GemmLaunch& la, int grid, hipStream_t st) {
 template <typename T, int KIND, int ACT>
 static void launch_bn(const GemmLaunch& la, int bn, int grid, hipStream_t st) {
   if (bn == 256) launch_t<T, KIND, ACT, 256>(la, grid, st);
+  else if (bn == 192) launch_t<T, KIND, ACT, 192>(la, grid, st);
   else launch_t<T, KIND, ACT, 128>(la, grid, st);
 }
 

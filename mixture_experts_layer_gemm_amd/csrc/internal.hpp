@@ -77,8 +77,8 @@ struct ECArgs {
   const float* keys;       // logits or probabilities [S,E]
   float* probs;            // [S,E] out (nullable)
   float* pT;               // scratch [E,S]
-  uint32_t* tok_mask;      // scratch [S, mask_words]
-  int32_t* tok_rows_tmp;   // scratch [S,E]
+  int32_t* tok_rows_tmp;   // scratch [E,S]: the token's row for the expert, or -1
+  int32_t* tok_cnt;        // scratch [S]: experts that took the token
   int32_t* counts;         // [E]
   int32_t* offsets;        // [E+1]
   int32_t* row_token;      // [E*C]
