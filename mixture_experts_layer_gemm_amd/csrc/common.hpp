@@ -22,11 +22,14 @@ typedef uint16_t bf16_t;
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 // fp32 -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even: the hardware conversion (v_cvt_pk_bf16_f32 on gfx950)
+typedef __bf16 hw_bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float hw_f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  const hw_f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, hw_bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return (bf16_t)(pack2_bf16(f, 0.f) & 0xFFFFu); }
 
 template <typename T> struct Elem;
 template <> struct Elem<bf16_t> {
@@ -55,10 +58,10 @@ __device__ __forceinline__ void unpack16(const uint4 v, float* out, float) {
 }
 __device__ __forceinline__ uint4 pack16(const float* in, bf16_t) {
   uint4 v;
-  v.x = (uint32_t)f32_to_bf16(in[0]) | ((uint32_t)f32_to_bf16(in[1]) << 16);
-  v.y = (uint32_t)f32_to_bf16(in[2]) | ((uint32_t)f32_to_bf16(in[3]) << 16);
-  v.z = (uint32_t)f32_to_bf16(in[4]) | ((uint32_t)f32_to_bf16(in[5]) << 16);
-  v.w = (uint32_t)f32_to_bf16(in[6]) | ((uint32_t)f32_to_bf16(in[7]) << 16);
+  v.x = pack2_bf16(in[0], in[1]);
+  v.y = pack2_bf16(in[2], in[3]);
+  v.z = pack2_bf16(in[4], in[5]);
+  v.w = pack2_bf16(in[6], in[7]);
   return v;
 }
 __device__ __forceinline__ uint4 pack16(const float* in, float) {
@@ -89,19 +92,23 @@ enum { ACT_GELU = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// erf by the rational approximation of Abramowitz & Stegun, Handbook of Mathematical Functions,
-// formula 7.1.26 (|error| <= 1.5e-7): erf(x) = 1 - (a1 t + ... + a5 t^5) e^{-x^2}, t = 1/(1 + p x),
-// x >= 0, odd extension for x < 0. Far below the bf16 rounding of the stored activation.
+// erf by the approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.28 (|error| <= 3e-7): erf(x) = 1 - (1 + a1 x + ... + a6 x^6)^-16 for x >= 0, odd extension
+// for x < 0. One reciprocal and no exponential; in fp32 the GELU built on it is within 1e-6 of
+// the exact function, far below the bf16 rounding of the stored activation.
 __device__ __forceinline__ float erf_as(float x) {
   const float ax = fabsf(x);
-  const float t = fast_rcp(fmaf(0.3275911f, ax, 1.0f));
-  float y = fmaf(1.061405429f, t, -1.453152027f);
-  y = fmaf(y, t, 1.421413741f);
-  y = fmaf(y, t, -0.284496736f);
-  y = fmaf(y, t, 0.254829592f);
-  y = y * t;
-  const float e = 1.0f - y * fast_exp(-ax * ax);
-  return copysignf(e, x);
+  float p = fmaf(0.0000430638f, ax, 0.0002765672f);
+  p = fmaf(p, ax, 0.0001520143f);
+  p = fmaf(p, ax, 0.0092705272f);
+  p = fmaf(p, ax, 0.0422820123f);
+  p = fmaf(p, ax, 0.0705230784f);
+  p = fmaf(p, ax, 1.0f);
+  p = p * p;
+  p = p * p;
+  p = p * p;
+  p = p * p;   // (...)^16; overflows to inf for large x, whose reciprocal is 0
+  return copysignf(1.0f - fast_rcp(p), x);
 }
 __device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f)); }
 // tanh form: 0.5 z (1 + tanh(u)) = z - z / (1 + e^{2u}), u = sqrt(2/pi) (z + 0.044715 z^3)

@@ -441,8 +441,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
         if (n >= P.N) continue;
         if (sizeof(T) == 2) {
           uint2 v;
-          v.x = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-          v.y = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+          v.x = pack2_bf16(h[0], h[1]);
+          v.y = pack2_bf16(h[2], h[3]);
           *reinterpret_cast<uint2*>(crow + n) = v;
         } else {
           *reinterpret_cast<float4*>(crow + n) = make_float4(h[0], h[1], h[2], h[3]);

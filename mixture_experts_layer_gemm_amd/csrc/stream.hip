@@ -134,8 +134,8 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
           T* c = (T*)P.C + orow * P.ldc + n;
           if (sizeof(T) == 2) {
             uint2 v;
-            v.x = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-            v.y = (uint32_t)f32_to_bf16(h[2]) | ((uint32_t)f32_to_bf16(h[3]) << 16);
+            v.x = pack2_bf16(h[0], h[1]);
+            v.y = pack2_bf16(h[2], h[3]);
             *reinterpret_cast<uint2*>(c) = v;
           } else {
             *reinterpret_cast<float4*>(c) = make_float4(h[0], h[1], h[2], h[3]);
