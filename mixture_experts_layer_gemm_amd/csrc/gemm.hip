@@ -47,38 +47,6 @@ struct GemmLaunch {
 // of 16 consecutive rows then cover all 64 banks once.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
-
-// 16 bytes per lane from global memory (wave-uniform base + per-lane byte offset) straight into
-// LDS: lane l of the wave writes LDS[lds_addr + 16*l]; lds_addr is the same for the whole wave (M0). Completion is tracked by
-// the wave's vmcnt, which the K loop waits on explicitly (wait_vmem) before a stage is read. The
-// instruction is issued from inline assembly so the compiler does not add its own wait for every
-// LDS DMA in flight before each LDS read (it cannot tell the ring's stages apart). Nothing else
-// in these kernels uses M0.
-__device__ __forceinline__ void gload_lds16(const void* base, uint32_t lane_off, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(lane_off), "s"(base),
-               "s"(lds_addr)
-               : "memory", "m0");
-}
-// LDS byte address of a __shared__ object.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(const lds_u8_t*)p; }
-// Wait until at most N of this wave's global loads (including loads into LDS) are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
-}
-// Workgroup barrier for the LDS ring. Every wave has already waited for its own loads of the
-// stage it needs (wait_vmem) and for its LDS reads (lgkmcnt 0), so no memory fence is needed (a
-// fence would also wait for the stages still in flight). The empty asm statements keep the
-// compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
 // Map m-tile `mt` of problem P to (group, first row, rows). Returns false for a tile past the end.
 // Number of m-tiles of a problem: the sum over groups of ceil(rows / kBM). Called by one whole wave;
 // the result is wave-uniform.

@@ -150,6 +150,180 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Ring streaming (bf16). A workgroup of 4 waves owns 64 weight rows (64 more gate rows with SwiGLU)
+// of one active expert; wave w takes the K stages w, w + 4, w + 8, ... (one MFMA K step, 64 bytes
+// of every row, per stage), so the four waves read neighbouring 64-byte pieces of each row at the
+// same time. Each wave streams its stages, weight rows and the 32 token rows of the pass alike,
+// through a private ring of kRingSlots LDS slots with direct global->LDS loads, kRingSlots - 1
+// stages in flight while one is multiplied: no barrier inside the loop and no register staging.
+// The four partial sums are added in LDS in wave order at the end.
+constexpr int kRingRows = 64;    // weight rows per workgroup (x 2 with SwiGLU)
+constexpr int kRingSlots = 3;    // stages per wave ring
+constexpr int kRingRowB = 64;    // bytes of one row per stage
+constexpr int kRingStageK = 4 * kRingRowB / 2;   // K elements per round of the 4 waves (bf16)
+
+bool stream_ring_supported(int dtype, int N, int K) {
+  return dtype == 0 && N > 0 && N % kRingRows == 0 && K % kRingStageK == 0 &&
+         K / kRingStageK >= kRingSlots - 1;
+}
+
+// One 16-byte global->LDS load per lane from a per-lane 64-bit address; lane l writes
+// LDS[lds + 16 * l].
+__device__ __forceinline__ void gload_lds16_va(const void* addr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int KIND, int ACT>
+__global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
+  using T = bf16_t;
+  constexpr int EPC = Elem<T>::kPer16B;
+  constexpr int BK = kRingRowB / (int)sizeof(T);               // K elements per stage
+  constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
+  constexpr int RW = SWIGLU ? 2 * kRingRows : kRingRows;       // weight rows per stage
+  constexpr int SLOT = (RW + 32) * kRingRowB;                  // + 32 token rows
+  constexpr int LPS = RW / 16;                                  // weight loads per stage
+  constexpr int PER = LPS + 2;                                  // loads per stage
+  constexpr int NT = kRingRows / 16;                            // 16-column subtiles (= waves)
+  constexpr int NB = SWIGLU ? 2 * NT : NT;                      // weight fragments per stage
+  constexpr int D = kRingSlots;
+  static_assert(NT == 4, "one subtile per wave in the epilogue");
+  static_assert(4 * 2 * NB * 64 * 16 <= 4 * D * SLOT, "reduction fits in the ring");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][D][SLOT];
+  const GemmProblem& P = la_p;
+  const int e = __builtin_amdgcn_readfirstlane(locate_active(P, blockIdx.y));
+  if (e < 0) return;
+  const int beg = P.offsets[e];
+  const int cnt = P.offsets[e + 1] - beg;
+  if (cnt <= 0) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int fr = lane & 15, fg = lane >> 4;
+  const int n0 = blockIdx.x * kRingRows;
+  // a load fills 16 rows of a slot: lane l writes row l/4 at position l%4, which holds the row's
+  // 16-byte chunk (l%4) ^ ((row/4)%4); readers undo the swizzle with swz()
+  const int rr = lane >> 2;
+  const int cc = (lane & 3) ^ ((rr >> 2) & 3);
+  const uint32_t lane_off = (uint32_t)(((size_t)rr * P.ldb + cc * EPC) * sizeof(T));
+  const T* Wb = (const T*)P.B + (size_t)e * P.b_gstride + (size_t)n0 * P.ldb;
+  const T* W3b = SWIGLU ? (const T*)P.B3 + (size_t)e * P.b_gstride + (size_t)n0 * P.ldb : Wb;
+  const int ns = P.K / kRingStageK;   // stages of every wave
+  uint8_t* myring = &ring[wave][0][0];
+  const uint32_t ring_lds = lds_addr(myring);
+  auto swz = [](int row, int chunk) { return row * kRingRowB + ((chunk ^ ((row >> 2) & 3)) << 4); };
+  const T* A = (const T*)P.A;
+
+  for (int t0 = 0; t0 < cnt; t0 += 32) {
+    const T* xr[2];   // this lane's token row (clamped to the expert's rows) and chunk, per group
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int r = beg + min(t0 + g * 16 + rr, cnt - 1);
+      const int src = P.a_rows ? P.a_rows[r] : r;
+      xr[g] = A + (size_t)src * P.lda + cc * EPC + (size_t)wave * BK;
+    }
+    auto issue = [&](int s) {
+      const int sl = s % D;
+      const size_t k = (size_t)(s * 4 + wave) * BK;
+      const uint32_t dst = ring_lds + sl * SLOT;
+#pragma unroll
+      for (int i = 0; i < LPS; ++i) {
+        const T* base = (i < NT ? Wb : W3b) + (size_t)(i % NT) * 16 * P.ldb + k;
+        gload_lds16(base, lane_off, dst + i * 16 * kRingRowB);
+      }
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        gload_lds16_va(xr[g] + (size_t)s * 4 * BK, dst + (RW + g * 16) * kRingRowB);
+    };
+    floatx4_t acc[2][NB];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[g][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int s) {
+      const uint8_t* sp = myring + (s % D) * SLOT;
+      uint4 bf[NB], xv[2];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) bf[i] = *reinterpret_cast<const uint4*>(sp + swz(i * 16 + fr, fg));
+#pragma unroll
+      for (int g = 0; g < 2; ++g) xv[g] = *reinterpret_cast<const uint4*>(sp + swz(RW + g * 16 + fr, fg));
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < NB; ++i) acc[g][i] = mfma16(bf[i], xv[g], acc[g][i], T());
+    };
+    static_assert(D == 3, "the tail below drains a 3-slot ring");
+    issue(0);
+    issue(1);
+    // stage s: wait for it (stage s + 1 stays in flight) and for the LDS reads of stage s - 1,
+    // refill that slot with stage s + 2, multiply
+    for (int s = 0; s + 2 < ns; ++s) {
+      __builtin_amdgcn_s_waitcnt((PER & 15) | (((PER >> 4) & 3) << 14) | (7 << 4));   // + lgkmcnt(0)
+      asm volatile("" ::: "memory");
+      issue(s + 2);
+      compute(s);
+    }
+    wait_vmem<PER>();
+    asm volatile("" ::: "memory");
+    compute(ns - 2);
+    wait_vmem<0>();
+    asm volatile("" ::: "memory");
+    compute(ns - 1);
+    // add the four waves' partial sums in wave order; wave w finishes subtile w
+    __syncthreads();
+    floatx4_t* red = reinterpret_cast<floatx4_t*>(&ring[0][0][0]);   // [wave][g][NB][64]
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < NB; ++i) red[((wave * 2 + g) * NB + i) * 64 + lane] = acc[g][i];
+    __syncthreads();
+    const int nt = wave;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      floatx4_t u = floatx4_t{0.f, 0.f, 0.f, 0.f}, gt = u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const floatx4_t a = red[((w * 2 + g) * NB + nt) * 64 + lane];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) u[t] += a[t];
+        if (SWIGLU) {
+          const floatx4_t b = red[((w * 2 + g) * NB + NT + nt) * 64 + lane];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) gt[t] += b[t];
+        }
+      }
+      // lane holds columns n0 + nt*16 + 4*fg + t of row t0 + g*16 + fr
+      const int rl = t0 + g * 16 + fr;
+      if (rl >= cnt) continue;
+      const int64_t orow = beg + rl;
+      const int n = n0 + nt * 16 + 4 * fg;
+      if (KIND == GEMM_UP) {
+        float h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          if (SWIGLU) h[t] = silu(gt[t]) * u[t];
+          else if (ACT == ACT_GELU_TANH) h[t] = gelu_tanh(u[t]);
+          else h[t] = gelu_erf(u[t]);
+        }
+        uint2 v;
+        v.x = pack2_bf16(h[0], h[1]);
+        v.y = pack2_bf16(h[2], h[3]);
+        *reinterpret_cast<uint2*>((T*)P.C + orow * P.ldc + n) = v;
+      } else {
+        *reinterpret_cast<float4*>((float*)P.C + orow * P.ldc + n) = make_float4(u[0], u[1], u[2], u[3]);
+      }
+    }
+    __syncthreads();   // the ring is reused by the next pass
+  }
+}
+
+template <int KIND, int ACT>
+static void ring_t(const GemmProblem& la, int max_active, hipStream_t st) {
+  const dim3 grid(la.N / kRingRows, max_active);
+  auto kfn = k_stream_ring<KIND, ACT>;
+  MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+}
+
 bool stream_gemm_supported(int dtype, int kind, int act, int N, int K) {
   const int step = dtype == 0 ? 128 : 64;   // K elements per block
   (void)kind;
@@ -186,6 +360,13 @@ static void launch_stream_t(const GemmProblem& la, int kind, int act, int max_ac
 
 hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, hipStream_t st) {
   if (max_active <= 0 || !p.offsets) return hipSuccess;
+  if (stream_ring_supported(dtype, p.N, p.K) && p.k_seg == p.K) {
+    if (kind == GEMM_DOWN) ring_t<GEMM_DOWN, ACT_GELU>(p, max_active, st);
+    else if (act == ACT_SWIGLU) ring_t<GEMM_UP, ACT_SWIGLU>(p, max_active, st);
+    else if (act == ACT_GELU_TANH) ring_t<GEMM_UP, ACT_GELU_TANH>(p, max_active, st);
+    else ring_t<GEMM_UP, ACT_GELU>(p, max_active, st);
+    return hipGetLastError();
+  }
   if (dtype == 0) launch_stream_t<bf16_t>(p, kind, act, max_active, st);
   else launch_stream_t<float>(p, kind, act, max_active, st);
   return hipGetLastError();

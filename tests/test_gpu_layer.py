@@ -91,6 +91,18 @@ def test_des_layer_full_size(name):
     _layer_case(spec, flags=moe.MOE_F_FORCE_TILED)
 
 
+@pytest.mark.parametrize("d,f,act,S", [
+    (256, 256, "swiglu", 32),       # up: 2 stages per wave (the ring's minimum); down: 2
+    (384, 640, "swiglu", 40),       # odd stage counts (3 and 5)
+    (256, 128, "gelu", 32),         # down K=128 is below the ring's minimum: register streaming
+    (512, 256, "gelu_tanh", 24),
+    (256, 384, "gelu", 200),        # many rows per expert: several 32-row passes
+])
+def test_stream_shapes(d, f, act, S):
+    spec = WORKLOADS["des_vote_b025"].replace(S=S, d=d, f=f, act=act)
+    _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
+
+
 def test_light_experts_only_layer():
     """No heavy experts: identity, zero and constant experts plus a shared expert."""
     spec = WORKLOADS["mmoe"].replace(S=500, d=256, f=512, E_heavy=0)
