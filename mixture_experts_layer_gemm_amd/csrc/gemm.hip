@@ -9,12 +9,14 @@
 // over the K-concatenation of their hidden activations).
 //
 // Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 192, 256}; each wave
-// owns 128 rows x BN/2 weight rows, which keeps LDS reads at 2/3 of a 128 x 64 split):
-//   * K advances 128 bytes per stage (64 bf16 / 32 fp32); A and B stages are double-buffered in
-//     LDS (2 x (32 KB + BN*128 B)) and filled by direct global->LDS loads (no staging registers),
-//     one barrier per stage; stage k+1's loads are in flight while stage k feeds the MFMAs.
-//   * LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), so the
-//     16-byte fragment reads of 16 consecutive rows hit distinct banks.
+// owns 128 token rows x BN/2 weight rows, the 2 x 2 split with the fewest LDS reads per MFMA):
+//   * K advances one MFMA K step (64 bytes of every tile row) per stage. Stages go through a ring
+//     of five LDS slots, filled by direct global->LDS loads (no staging registers): four stages
+//     are in flight while one feeds the MFMAs, which hides L2-miss latency; one barrier per stage.
+//   * The loads of a stage and the LDS fragment reads of the next one are spread between the
+//     MFMAs of the current one (sched_group_barrier regions), so issue never stalls on a full queue.
+//   * LDS rows are 64 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 2) & 3), so the 16-byte
+//     fragment reads of 16 consecutive rows cover all banks once.
 //   * Weights are MFMA operand P and tokens operand Q, so each lane ends with 4 consecutive output
 //     columns of one row: 8-byte (bf16) / 16-byte (fp32) stores.
 //   * Gather fused into the A loads: row r reads x[row_token[r]].
@@ -31,7 +33,7 @@ namespace moe {
 
 constexpr int kBM = 256;
 constexpr int kRowB = 64;           // bytes of one tile row per stage (one MFMA K-step)
-constexpr int kStages = 4;          // LDS ring: three stages in flight while one is consumed
+constexpr int kStages = 5;          // LDS ring: four stages in flight while one is consumed
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
 constexpr int kWaves = 4;           // 2 x 2 wave grid, one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -64,7 +66,9 @@ __device__ __forceinline__ int count_mtiles(const GemmProblem& P, int lane) {
   return total;
 }
 
-__device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& g, int& row0, int& rows) {
+// s_res: 3 ints of LDS.
+__device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int* s_res, int& g, int& row0,
+                                             int& rows) {
   if (!P.offsets) {
     const int mpg = (P.M_uni + kBM - 1) / kBM;
     if (mpg == 0) return false;
@@ -75,7 +79,6 @@ __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int& 
     rows = min(kBM, P.M_uni - row0);
     return true;
   }
-  __shared__ int s_res[3];
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int carry = 0;
@@ -176,11 +179,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int LPS = A_LD + B_LD;                       // loads per wave per stage
   // One array per ring stage: with the K loop unrolled by kStages every LDS access names its stage
   // at compile time.
-  static_assert(kStages == 4, "the ring below is written for four stages");
+  static_assert(kStages == 5, "the ring below is written for five stages");
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem2[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem3[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem4[STAGE];
+  // The decode's few shared ints live in the last ring slot (five 32 KB slots are all of LDS); a
+  // barrier after the decode orders their last reads before the first load into that slot.
+  int* const s_mt = reinterpret_cast<int*>(smem4);
+  int* const s_res = s_mt + 2;
 
   // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
   // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
@@ -188,7 +196,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   // weight panels and token panels in one L2. An XCD runs its chunk of problem 0 (the one with the
   // longer K, placed there by the host) and then its chunk of problem 1; workgroups beyond both
   // chunks (the grid is sized from upper bounds on the row counts) exit at once.
-  __shared__ int s_mt[2];
   if (threadIdx.x < 64) {
     const int m0 = count_mtiles(args.p0, threadIdx.x);
     const int m1 = args.slots1 ? count_mtiles(args.p1, threadIdx.x) : 0;
@@ -213,7 +220,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   const int mt = grp * kGM + rem % gsz;
   const int nt = rem / gsz;
   int g, row0, rows;
-  if (!locate_mtile(P, mt, g, row0, rows)) return;
+  if (!locate_mtile(P, mt, s_res, g, row0, rows)) return;
+  __syncthreads();   // every wave has read s_mt and s_res
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   };
 
   // One K step t, after the barrier: MFMAs on the fragments of stage t (cur) with, spread between
-  // them, the LDS reads of stage t + 1 (into nxt) and the loads of stage t + 4 (into the LDS slot
+  // them, the LDS reads of stage t + 1 (into nxt) and the loads of stage t + 5 (into the LDS slot
   // of stage t, free once every wave has passed the barrier). Issued as blocks, the LDS reads would
   // fill the LDS queue and the loads the memory queue, stalling the wave before its MFMAs (issue is
   // in order). Loads are inline assembly, which the scheduler does not move, so the step is a chain
@@ -359,29 +367,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
       SS::template region<SS::load_pos(LPS - 1), NM>();
     }
   };
-  // step t: wait for stage t + 1 (stages t + 2, t + 3 may stay in flight), synchronise, then the body.
+  // step t: wait for stage t + 1 (stages t + 2 .. t + 4 may stay in flight), synchronise, then the
+  // body.
   auto step = [&](const uint8_t* next, uint32_t refill, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): cur is in registers
-    wait_vmem<2 * LPS>();
+    wait_vmem<3 * LPS>();
     ring_barrier();
     const Dma dma = next_dma(refill);
     body(body, std::integral_constant<int, 0>{}, next, dma, cur, nxt);
   };
 
   uint4 fa[NF], fb[NF];
-  const uint32_t l0 = lds_addr(smem0), l1 = lds_addr(smem1), l2 = lds_addr(smem2), l3 = lds_addr(smem3);
+  const uint32_t l0 = lds_addr(smem0), l1 = lds_addr(smem1), l2 = lds_addr(smem2), l3 = lds_addr(smem3),
+                 l4 = lds_addr(smem4);
   issue_all(next_dma(l0));
   issue_all(next_dma(l1));
   issue_all(next_dma(l2));
   issue_all(next_dma(l3));
-  wait_vmem<3 * LPS>();
+  issue_all(next_dma(l4));
+  wait_vmem<4 * LPS>();
   ring_barrier();
   read_frags(smem0, fa);
-  for (int kt = 0; kt < nk; kt += kStages) {
+  // stage t sits in slot t % 5; the fragment buffers alternate, so ten steps bring both back
+  for (int kt = 0; kt < nk; kt += 2 * kStages) {
     step(smem1, l0, fa, fb);
     if (kt + 1 < nk) step(smem2, l1, fb, fa);
     if (kt + 2 < nk) step(smem3, l2, fa, fb);
-    if (kt + 3 < nk) step(smem0, l3, fb, fa);
+    if (kt + 3 < nk) step(smem4, l3, fb, fa);
+    if (kt + 4 < nk) step(smem0, l4, fa, fb);
+    if (kt + 5 < nk) step(smem1, l0, fb, fa);
+    if (kt + 6 < nk) step(smem2, l1, fa, fb);
+    if (kt + 7 < nk) step(smem3, l2, fb, fa);
+    if (kt + 8 < nk) step(smem4, l3, fa, fb);
+    if (kt + 9 < nk) step(smem0, l4, fb, fa);
   }
   wait_vmem<0>();   // no load into LDS may still be in flight when the workgroup ends
 
