@@ -324,7 +324,7 @@ moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const voi
   void* H = w + p.o_h;
   void* Hs = w + p.o_hs;
   GemmProblem up[2], dn[2];
-  int64_t ub[2];
+  int64_t ub[2], mth[2] = {0, 0};
   int nup = 0;
   if (d->E_heavy > 0) {
     GemmProblem u{};
@@ -367,6 +367,10 @@ moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const voi
       up[nup] = u;
       dn[nup] = v;
       ub[nup] = p.R_max;
+      // expected 256-row tiles: expert choice fills every expert to C rows; otherwise about half a
+      // ragged tile per expert on top of the rows
+      mth[nup] = d->mode == MOE_EXPERT_CHOICE ? (int64_t)d->E_heavy * ((p.C + 255) / 256)
+                                                : (p.R_max + 255) / 256 + d->E_heavy / 2;
       ++nup;
     }
   }
@@ -415,8 +419,8 @@ moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const voi
     ++nup;
   }
   if (nup > 0) {
-    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_UP, d->act, up, ub, nup, st), d, st));
-    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_DOWN, d->act, dn, ub, nup, st), d, st));
+    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_UP, d->act, up, ub, mth, nup, st), d, st));
+    MOE_TRY(after_launch(launch_grouped_gemm(d->dtype, GEMM_DOWN, d->act, dn, ub, mth, nup, st), d, st));
   }
   return MOE_OK;
 }

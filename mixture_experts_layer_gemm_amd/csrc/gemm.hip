@@ -24,6 +24,8 @@
 //     contiguous range, swept as 8 m-tiles x all n-tiles, which keeps an expert's weight panels and
 //     token panels in one XCD's L2.
 //   * The expert of an m-tile comes from a wave-wide scan of ceil(count_e / 256) over experts.
+#include <algorithm>
+#include <cmath>
 #include <type_traits>
 
 #include "common.hpp"
@@ -448,24 +450,63 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 
 static int out_cols_per_tile(int kind, int act, int BN) { return (kind == GEMM_UP && act == ACT_SWIGLU) ? BN / 2 : BN; }
 
-// The 256-row weight tile keeps LDS reads per MFMA lower than the 128-row one, so it is used
-// unless padding N up to whole tiles would waste more than 1/8 of the work.
-// Tile width: 256 unless that pads N by more than 1/8; then 192 if it pads less than 256 does,
-// else 128. (256 reads the fewest bytes per FLOP; 192 fits N = 4.5 x 256 exactly.)
-static int pick_bn(int kind, int act, int N) {
-  if (N <= 0 || N % 64 != 0) return 0;
-  auto padded = [&](int bn) {
+// Tile width. The time of a launch is modelled as (rounds of one tile per compute unit) x (time of
+// one tile), with the time of a tile proportional to BN / eff(BN): the wider tile reads fewer LDS
+// bytes per MFMA (measured dense rates: eff = 1, 0.9, 0.74 for BN = 256, 192, 128), the narrower
+// ones make more tiles, which can fill the last round better. A problem's tiles count K / K_min
+// rounds each, K_min the shortest K of the launch.
+static int tile_cost(int bn) { return bn == 256 ? 256 : bn == 192 ? 213 : 173; }
+
+static int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// m-tiles of a problem: exact for uniform groups; for offsets-based groups the caller's hint, else
+// the count for rows_ub rows plus half a ragged tile per group.
+static int64_t est_mtiles(const GemmProblem& p, int64_t rows_ub, const int64_t* hint) {
+  if (!p.offsets) return (int64_t)p.G * ((p.M_uni + kBM - 1) / kBM);
+  if (hint && *hint > 0) return *hint;
+  return std::max<int64_t>(1, (rows_ub + kBM - 1) / kBM + p.G / 2);
+}
+
+static int pick_bn(int kind, int act, const GemmProblem* probs, const int64_t* rows_ub, const int64_t* mt_hint,
+                   int nprob) {
+  for (int i = 0; i < nprob; ++i)
+    if (probs[i].N <= 0 || probs[i].N % 64 != 0) return 0;
+  int kmin = probs[0].K;
+  for (int i = 0; i < nprob; ++i) kmin = std::min(kmin, probs[i].K);
+  kmin = std::max(kmin, 1);
+  const int64_t cus = compute_units();
+  int best = 0;
+  double best_t = 0.0;
+  for (int bn : {256, 192, 128}) {
     const int c = out_cols_per_tile(kind, act, bn);
-    return ((int64_t)N + c - 1) / c * c;
-  };
-  if (padded(256) * 8 <= (int64_t)N * 9) return 256;
-  if (padded(192) < padded(256) && padded(192) * 8 <= (int64_t)N * 9) return 192;
-  return 128;
+    double units = 0.0;   // tiles, weighted by K / kmin (a round is one tile of the shortest K)
+    for (int i = 0; i < nprob; ++i)
+      units += (double)est_mtiles(probs[i], rows_ub[i], mt_hint ? mt_hint + i : nullptr) *
+               ((probs[i].N + c - 1) / c) * probs[i].K / kmin;
+    const double t = std::ceil(units / (double)cus - 1e-9) * tile_cost(bn);
+    if (best == 0 || t < best_t) {
+      best = bn;
+      best_t = t;
+    }
+  }
+  return best;
 }
 
 bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K) {
+  (void)kind;
+  (void)act;
   const int bk = kRowB / (dtype == 0 ? 2 : 4);
-  return N > 0 && K > 0 && K % bk == 0 && pick_bn(kind, act, N) != 0;
+  return N > 0 && N % 64 == 0 && K > 0 && K % bk == 0;
 }
 
 template <typename T, int KIND, int ACT, int BN>
@@ -495,9 +536,9 @@ static void launch_kind(const GemmLaunch& la, int kind, int act, int bn, int gri
 }
 
 hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* probs, const int64_t* rows_ub,
-                               int nprob, hipStream_t st) {
+                               const int64_t* mt_hint, int nprob, hipStream_t st) {
   if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
-  const int bn = pick_bn(kind, act, probs[0].N);
+  const int bn = pick_bn(kind, act, probs, rows_ub, mt_hint, nprob);
   if (bn == 0) return hipErrorInvalidValue;
   // the problem with the longer K goes first (see the tile decode in the kernel)
   const int first = (nprob == 2 && probs[1].K > probs[0].K) ? 1 : 0;
@@ -505,7 +546,6 @@ hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* 
   int64_t total = 0;
   for (int n = 0; n < nprob; ++n) {
     const int i = n == 0 ? first : 1 - first;
-    if (pick_bn(kind, act, probs[i].N) != bn) return hipErrorInvalidValue;
     const int c = out_cols_per_tile(kind, act, bn);
     const int64_t tiles_n = (probs[i].N + c - 1) / c;
     int64_t mt;

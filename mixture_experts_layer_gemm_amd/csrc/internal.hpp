@@ -133,9 +133,10 @@ struct GemmProblem {
 };
 enum { GEMM_UP = 0, GEMM_DOWN = 1 };
 // kind GEMM_UP: C (dtype) = act(A.B^T) (SwiGLU: silu(A.B3^T) * (A.B^T)); GEMM_DOWN: C (fp32) = A.B^T.
-// `rows_ub[i]` bounds the total rows of problem i (for the grid).
+// `rows_ub[i]` bounds the total rows of problem i (for the grid); `mt_hint[i]` (may be null) is the
+// expected number of 256-row tiles of problem i, used to choose the tile width.
 hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* probs, const int64_t* rows_ub,
-                               int nprob, hipStream_t st);
+                               const int64_t* mt_hint, int nprob, hipStream_t st);
 bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K);
 
 // Weight-streaming grouped GEMM for few rows per expert; grid.y = max_active bounds the number
