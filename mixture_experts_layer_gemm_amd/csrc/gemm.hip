@@ -51,26 +51,26 @@ struct GemmLaunch {
 // of 16 consecutive rows then cover all 64 banks once.
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-// Map m-tile `mt` of problem P to (group, first row, rows). Returns false for a tile past the end.
-// Number of m-tiles of a problem: the sum over groups of ceil(rows / kBM). Called by one whole wave;
-// the result is wave-uniform.
-__device__ __forceinline__ int count_mtiles(const GemmProblem& P, int lane) {
+// m-tiles of a problem: groups in order, ceil(rows_g / 256) tiles each. The group offsets are read
+// with scalar loads (constant address space: the kernel never writes them), so finding a tile's
+// group takes no vector registers and no vector-memory wait (those would also wait for the ring's
+// loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* scalar_i32_ptr;
+
+__device__ __forceinline__ int mtile_total(const GemmProblem& P) {
   if (!P.offsets) return P.G * ((P.M_uni + kBM - 1) / kBM);
-  int total = 0;
-  for (int g0 = 0; g0 < P.G; g0 += 64) {
-    const int gi = g0 + lane;
-    int mts = 0;
-    if (gi < P.G) mts = (P.offsets[gi + 1] - P.offsets[gi] + kBM - 1) / kBM;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mts += __shfl_xor(mts, o, 64);
-    total += mts;
+  const scalar_i32_ptr o = (scalar_i32_ptr)P.offsets;
+  int tot = 0, prev = o[0];
+  for (int g = 0; g < P.G; ++g) {
+    const int nx = o[g + 1];
+    tot += (nx - prev + kBM - 1) / kBM;
+    prev = nx;
   }
-  return total;
+  return tot;
 }
 
-// s_res: 3 ints of LDS.
-__device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int* s_res, int& g, int& row0,
-                                             int& rows) {
+// Group, first row and row count of m-tile `mt` (uniform). False past the end.
+__device__ __forceinline__ bool mtile_locate(const GemmProblem& P, int mt, int& g, int& row0, int& rows) {
   if (!P.offsets) {
     const int mpg = (P.M_uni + kBM - 1) / kBM;
     if (mpg == 0) return false;
@@ -81,48 +81,21 @@ __device__ __forceinline__ bool locate_mtile(const GemmProblem& P, int mt, int* 
     rows = min(kBM, P.M_uni - row0);
     return true;
   }
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    int carry = 0;
-    int found = 0, fg = -1, frow0 = 0, frows = 0;
-    for (int g0 = 0; g0 < P.G && !found; g0 += 64) {
-      const int gi = g0 + lane;
-      int beg = 0, cnt = 0;
-      if (gi < P.G) {
-        beg = P.offsets[gi];
-        cnt = P.offsets[gi + 1] - beg;
-      }
-      const int mts = (cnt + kBM - 1) / kBM;
-      int incl = mts;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
-      }
-      const int excl = carry + incl - mts;
-      const bool hit = gi < P.G && mt >= excl && mt < excl + mts;
-      const uint64_t m = __ballot(hit);
-      if (m) {
-        const int src = __ffsll((unsigned long long)m) - 1;
-        const int lm = __shfl(mt - excl, src, 64);
-        fg = g0 + src;
-        frow0 = __shfl(beg, src, 64) + lm * kBM;
-        frows = min(kBM, __shfl(beg + cnt, src, 64) - frow0);
-        found = 1;
-      }
-      carry += __shfl(incl, 63, 64);
+  const scalar_i32_ptr o = (scalar_i32_ptr)P.offsets;
+  int acc = 0, prev = o[0];
+  for (int gi = 0; gi < P.G; ++gi) {
+    const int nx = o[gi + 1];
+    const int mts = (nx - prev + kBM - 1) / kBM;
+    if (mt < acc + mts) {
+      g = gi;
+      row0 = prev + (mt - acc) * kBM;
+      rows = min(kBM, nx - row0);
+      return true;
     }
-    if (lane == 0) {
-      s_res[0] = found ? fg : -1;
-      s_res[1] = frow0;
-      s_res[2] = frows;
-    }
+    acc += mts;
+    prev = nx;
   }
-  __syncthreads();
-  g = s_res[0];
-  row0 = s_res[1];
-  rows = s_res[2];
-  return g >= 0;
+  return false;
 }
 
 // Placement of the work of one K step: NM MFMAs; NF LDS reads, read q right before MFMA
@@ -179,18 +152,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int A_LD = kBM / (kRowsPerLoad * kWaves);   // wave load instructions per stage
   constexpr int B_LD = BN / (kRowsPerLoad * kWaves);
   constexpr int LPS = A_LD + B_LD;                       // loads per wave per stage
-  // One array per ring stage: with the K loop unrolled by kStages every LDS access names its stage
-  // at compile time.
+  // One array per ring stage: with the K loop unrolled every LDS access names its stage at compile
+  // time. Five 32 KB slots are all of LDS; nothing else in the kernel uses LDS.
   static_assert(kStages == 5, "the ring below is written for five stages");
   __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem2[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem3[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t smem4[STAGE];
-  // The decode's few shared ints live in the last ring slot (five 32 KB slots are all of LDS); a
-  // barrier after the decode orders their last reads before the first load into that slot.
-  int* const s_mt = reinterpret_cast<int*>(smem4);
-  int* const s_res = s_mt + 2;
 
   // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
   // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
@@ -198,16 +167,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   // weight panels and token panels in one L2. An XCD runs its chunk of problem 0 (the one with the
   // longer K, placed there by the host) and then its chunk of problem 1; workgroups beyond both
   // chunks (the grid is sized from upper bounds on the row counts) exit at once.
-  if (threadIdx.x < 64) {
-    const int m0 = count_mtiles(args.p0, threadIdx.x);
-    const int m1 = args.slots1 ? count_mtiles(args.p1, threadIdx.x) : 0;
-    if (threadIdx.x == 0) {
-      s_mt[0] = m0;
-      s_mt[1] = m1;
-    }
-  }
-  __syncthreads();
-  const int live0 = s_mt[0] * args.tiles_n0, live1 = s_mt[1] * args.tiles_n1;
+  const int mtl0 = mtile_total(args.p0), mtl1 = args.slots1 ? mtile_total(args.p1) : 0;
+  const int live0 = mtl0 * args.tiles_n0, live1 = mtl1 * args.tiles_n1;
   const int c0 = (live0 + 7) >> 3, c1 = (live1 + 7) >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const bool second = slot >= c0;
@@ -215,15 +176,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   if (second ? (slot - c0 >= c1 || Lq >= live1) : Lq >= live0) return;
   const GemmProblem P = second ? args.p1 : args.p0;   // a copy: kept in scalar registers
   const int tn = second ? args.tiles_n1 : args.tiles_n0;
-  const int mt_live = second ? s_mt[1] : s_mt[0];
+  const int mt_live = second ? mtl1 : mtl0;
   const int grp = Lq / (kGM * tn);
   const int rem = Lq - grp * kGM * tn;
   const int gsz = min(kGM, mt_live - grp * kGM);
   const int mt = grp * kGM + rem % gsz;
   const int nt = rem / gsz;
   int g, row0, rows;
-  if (!locate_mtile(P, mt, s_res, g, row0, rows)) return;
-  __syncthreads();   // every wave has read s_mt and s_res
+  if (!mtile_locate(P, mt, g, row0, rows)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -261,7 +221,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   const int nk = P.K / BK;
   // Source positions of the next stage to load: K offset into A, and into B (whose K axis may be
   // split into segments of k_seg elements placed k_seg_stride apart). Stages are issued in order,
-  // one per K step; stages past the end re-load stage 0 (valid memory, never read).
+  // one per K step; stages past the end re-load the last stage (valid memory that the load just
+  // before brought into the caches; never read).
   const int k_seg = (int)P.k_seg;
   const int64_t k_skip = P.k_seg_stride - P.k_seg;
   int64_t a_k = 0, b_k = 0;
@@ -275,18 +236,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   };
   auto next_dma = [&](uint32_t stage) -> Dma {
     Dma d;
-    const bool live = issued < nk;
-    d.a = Ab + (live ? a_k : 0);
-    d.b = Bb + (live ? b_k : 0);
-    d.b3 = SWIGLU ? B3b + (live ? b_k : 0) : nullptr;
+    d.a = Ab + a_k;
+    d.b = Bb + b_k;
+    d.b3 = SWIGLU ? B3b + b_k : nullptr;
     d.lds = stage + wave_off;
-    ++issued;
-    a_k += BK;
-    b_k += BK;
-    b_within += BK;
-    if (b_within == k_seg) {
-      b_within = 0;
-      b_k += k_skip;
+    if (++issued < nk) {   // past the end the position stays on the last stage
+      a_k += BK;
+      b_k += BK;
+      b_within += BK;
+      if (b_within == k_seg) {
+        b_within = 0;
+        b_k += k_skip;
+      }
     }
     return d;
   };
