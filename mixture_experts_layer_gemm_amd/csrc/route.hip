@@ -531,49 +531,82 @@ __device__ __forceinline__ int float_order(float f) {
 }
 
 // Top-k of one token whose experts span the whole wave (expert e in lane e % 64, slot e / 64),
-// among experts allowed by `allow` (bit v of the lane's mask): k rounds of a wave-wide maximum
-// (a DPP reduction) and a ballot for the lowest expert index holding it. Same result as
-// token_topk<64, V>. Returns the lane's chosen-set bits; when out_e is given, the lane holding
-// the j-th chosen expert writes it and its probability to out_e[j], out_p[j] (key order).
+// among experts allowed by `allow` (bit v of the lane's mask), ranked by (key descending, expert
+// ascending): the same set and order as token_topk<64, V>. Instead of k rounds of a wave-wide
+// maximum, a radix select finds the k-th largest key with one ballot per bit (MSB first, stopping
+// as soon as exactly k keys reach the prefix); equal keys at the threshold go to the lowest
+// experts. Returns the lane's chosen-set bits; when out_e is given, the j-th chosen expert
+// (j = its rank among the chosen) and its probability go to out_e[j], out_p[j]. With fewer than k
+// eligible experts, all of them are chosen and the remaining out entries are left alone.
 template <int V>
 __device__ __forceinline__ unsigned wave_topk(const float (&key)[V], const float (&p)[V], unsigned allow, int E,
                                               int lane, int k, int* out_e, float* out_p) {
-  unsigned taken = 0;
-  int ord[V];
+  uint32_t u[V];   // keys as unsigned integers of the same order
+  bool el[V];
+  int n = 0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    ord[v] = float_order(key[v]);
-    if (!(lane + v * 64 < E && ((allow >> v) & 1u))) taken |= 1u << v;   // never eligible
+    u[v] = (uint32_t)float_order(key[v]) ^ 0x80000000u;
+    el[v] = lane + v * 64 < E && ((allow >> v) & 1u);
+    n += __popcll(__ballot(el[v]));
   }
-  for (int j = 0; j < k; ++j) {
-    int best = INT_MIN;
+  const int kq = min(k, n);
+  if (kq <= 0) return 0;
+  uint32_t T = 0;
+  bool exact = false;   // exactly kq keys are >= T
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = T | (1u << b);
+    int c = 0;
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (!((taken >> v) & 1u)) best = max(best, ord[v]);
-    const int m = __ockl_wfred_max_i32(best);
-    bool done = false;
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      if (!done) {
-        const uint64_t hit = __ballot(!((taken >> v) & 1u) && ord[v] == m);
-        if (hit) {
-          done = true;
-          const int l = __ffsll((unsigned long long)hit) - 1;
-          if (lane == l) {
-            taken |= 1u << v;
-            if (out_e) {
-              out_e[j] = v * 64 + l;
-              out_p[j] = p[v];
-            }
-          }
-        }
-      }
+    for (int v = 0; v < V; ++v) c += __popcll(__ballot(el[v] && u[v] >= cand));
+    if (c >= kq) T = cand;
+    if (c == kq) {
+      exact = true;
+      break;
     }
   }
-  // clear the never-eligible marks
+  unsigned taken = 0;
+  if (exact) {
 #pragma unroll
-  for (int v = 0; v < V; ++v)
-    if (!(lane + v * 64 < E && ((allow >> v) & 1u))) taken &= ~(1u << v);
+    for (int v = 0; v < V; ++v)
+      if (el[v] && u[v] >= T) taken |= 1u << v;
+  } else {
+    // T is the kq-th largest key: take the larger ones and the lowest experts holding T
+    int need = kq;
+#pragma unroll
+    for (int v = 0; v < V; ++v) need -= __popcll(__ballot(el[v] && u[v] > T));
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const uint64_t eq = __ballot(el[v] && u[v] == T);
+      const int r = __popcll(eq & lanemask_lt());
+      if (el[v] && (u[v] > T || (u[v] == T && r < need))) taken |= 1u << v;
+      need -= min(need, __popcll(eq));
+    }
+  }
+  if (out_e) {
+    // rank of each chosen expert: the chosen ones that come before it
+    int rank[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) rank[v] = 0;
+#pragma unroll
+    for (int vc = 0; vc < V; ++vc) {
+      uint64_t m = __ballot((taken >> vc) & 1u);
+      while (m) {
+        const int c = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const uint32_t tc = (uint32_t)__builtin_amdgcn_readlane((int)u[vc], c);
+        const int ec = vc * 64 + c;
+#pragma unroll
+        for (int v = 0; v < V; ++v) rank[v] += (tc > u[v] || (tc == u[v] && ec < v * 64 + lane)) ? 1 : 0;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if ((taken >> v) & 1u) {
+        out_e[rank[v]] = v * 64 + lane;
+        out_p[rank[v]] = p[v];
+      }
+  }
   return taken;
 }
 
@@ -661,20 +694,26 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       a.votes[e] = v;
     }
     lds_barrier();
-    // elect: rank of e under (vote desc, index asc), one wave-wide ballot per (e, 64 rivals)
-    for (int t = wave; t < E * ((E + 63) / 64); t += kSmallWaves) {
-      const int e = t % E, o = (t / E) * 64 + lane;
-      const float ve = s_votes[e];
-      bool before = false;
-      if (o < E) {
-        const float vo = s_votes[o];
-        before = vo > ve || (vo == ve && o < e);
+    // core: the M experts of largest vote (ties to the lower index). Expert e's rank is the number
+    // of experts before it in that order; the E x E comparisons are split over all threads (each
+    // expert gets kSmallThreads / E of them, adding partial counts into s_rank, zero from the start),
+    // and the core is then listed ascending by a prefix count over the membership flags.
+    {
+      const int per = max(1, kSmallThreads / E);   // threads per expert
+      const int span = (E + per - 1) / per;        // rivals per thread
+      for (int t = tid; t < E * per; t += kSmallThreads) {
+        const int e = t / per, part = t - e * per;
+        const float ve = s_votes[e];
+        const int o0 = part * span, o1 = min(E, o0 + span);
+        int r = 0;
+        for (int o = o0; o < o1; ++o) {
+          const float vo = s_votes[o];
+          r += (vo > ve || (vo == ve && o < e)) ? 1 : 0;
+        }
+        if (r) atomicAdd(&s_rank[e], r);
       }
-      const int c = __popcll(__ballot(before));
-      if (lane == 0) atomicAdd(&s_rank[e], c);
     }
     lds_barrier();
-    // core = experts of rank < M, listed ascending
     if (wave == 0) {
       int cbase = 0;
       for (int e0 = 0; e0 < E; e0 += 64) {
@@ -690,31 +729,30 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       }
     }
     lds_barrier();
-    // selection: top-kk inside the core
-    for (int base = 0; base < S; base += tpb) {
-      const int s = base + tid / LPT;
-      const bool live = s < S;
-      float key[V], p[V];
-      unsigned allow = 0;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = sub + v * LPT;
-        key[v] = (live && e < E) ? s_key[min(s, S - 1) * E + e] : -FLT_MAX;
-        p[v] = (live && e < E) ? s_p[min(s, S - 1) * E + e] : 0.f;
-        if (e < E && s_rank[e] < M) allow |= 1u << v;
+    // selection: the top kk of each token inside the core. The keys of each token's core experts
+    // are first gathered as order-preserving integers (s_aux, free again); lane (token s, core slot
+    // c) then ranks its expert among them (key descending; the core is ascending, so ties go to the
+    // lower slot) and, if the rank is below kk, writes the slot of that rank.
+    int* s_ord = reinterpret_cast<int*>(s_aux);   // [S][M]
+    for (int t = tid; t < S * M; t += kSmallThreads) {
+      const int s = t / M, c = t - s * M;
+      s_ord[t] = float_order(s_key[s * E + s_core[c]]);
+    }
+    lds_barrier();
+    for (int t = tid; t < S * M; t += kSmallThreads) {
+      const int s = t / M, c = t - s * M;
+      const int* os = s_ord + s * M;
+      const int oc = os[c];
+      int r = 0;
+#pragma unroll 8
+      for (int c2 = 0; c2 < M; ++c2) {
+        const int o2 = os[c2];
+        r += (o2 > oc || (o2 == oc && c2 < c)) ? 1 : 0;
       }
-      if constexpr (LPT == 64) {
-        wave_topk<V>(key, p, allow, E, lane, kk, live ? s_idx + s * kk : nullptr, s_w + s * kk);
-      } else {
-        int sel_e[kMaxK];
-        float sel_p[kMaxK];
-        token_topk<LPT, V>(key, p, allow, E, sub, lane, kk, sel_e, sel_p);
-        if (live && sub == 0) {
-          for (int j = 0; j < kk; ++j) {
-            s_idx[s * kk + j] = sel_e[j];
-            s_w[s * kk + j] = sel_p[j];
-          }
-        }
+      if (r < kk) {
+        const int ec = s_core[c];
+        s_idx[s * kk + r] = ec;
+        s_w[s * kk + r] = s_p[s * E + ec];
       }
     }
     lds_barrier();
