@@ -287,14 +287,21 @@ def cpu_baseline(spec, inp, n_tokens):
             h, prev = r["y"], r["logits"]
         return time.perf_counter() - t
 
+    target = 12.0   # seconds of oracle work
     if n_tokens <= 0:
         n0 = min(spec.S, 128)
         t0 = run(n0)
-        n_tokens = int(min(spec.S, max(n0, n0 * 12.0 / max(t0, 1e-3))))
+        n_tokens = int(min(spec.S, max(n0, n0 * target / max(t0, 1e-3))))
     n_tokens = min(n_tokens, spec.S)
-    t = run(n_tokens)
-    return {"value": round(n_tokens / t, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n_tokens} of {spec.S} tokens, whole layer ({spec.n_layers} layer(s)), numpy fp64",
+    # the first n tokens, repeated until about `target` seconds have passed when one pass is short
+    t, reps = 0.0, 0
+    while reps == 0 or (t < target and t / reps < target / 2 and reps < 50):
+        t += run(n_tokens)
+        reps += 1
+    rep_note = f", {reps} passes" if reps > 1 else ""
+    return {"value": round(n_tokens * reps / t, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} of {spec.S} tokens{rep_note}, whole layer ({spec.n_layers} layer(s)), "
+                      f"numpy fp64",
             "seconds": round(t, 2)}
 
 
