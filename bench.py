@@ -37,6 +37,8 @@ DESCRIPTIONS = {
     "ec_dit": "64 x 128 = 8192 tokens, d=1536, 32 GELU experts 1536->6144->1536, expert choice C=512",
     "des_vote_b025": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 16",
     "des_vote_b050": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 32",
+    "des_seq": "DES-Seq decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, each token its own "
+               "top-8 (experts loaded = their union)",
     "mmoe": "MMOE MoE++ stack: 64 x 256 = 16384 tokens, d=1152, 16 GELU experts + identity/zero/constant + 1 shared, "
             "top-2 with gate residual, 4 layers",
 }
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="dit_moe_xl", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
+    ap.add_argument("--des-fit", action="store_true",
+                    help="fit the DES per-expert latency model f(c) = a*c + b on the streaming kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -68,6 +72,83 @@ def calibrate_copy():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 3}), flush=True)
+
+
+def des_fit(args):
+    """The DES latency model ("Dynamic Expert Sharing", 2.1): an expert that serves c rows costs
+    f(c) = a*c + b, b being the fetch of its weights, so a block costs a*(rows) + b*(experts used).
+    Decode blocks of N in {8, 16, 32, 64} tokens are routed by DES-Vote (core 16 and 32) and by
+    DES-Seq (each token its own top-8: the experts used are the union); the two streaming kernels'
+    time per block (HIP events on their launches) is fitted by least squares to
+    t = a*rows + b*experts + c0 (c0: the fixed cost of the two launches). Prints one JSON line per
+    block and one with the fit."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_gemm_amd as moe
+    from synth import WORKLOADS, gen_layer_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = WORKLOADS["des_vote_b025"].replace(S=64)
+    inp = gen_layer_inputs(base, seed=0)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    copies = []
+    for _ in range(4):   # rotated so the 256 MB MALL cannot keep a block's experts between calls
+        t = {"w_router": up(inp.bits["w_router.0"]), "w1": up(inp.bits["w1.0"]), "w2": up(inp.bits["w2.0"]),
+             "w3": up(inp.bits["w3.0"])}
+        copies.append((t, moe.weights_struct(t)))
+    x_all = up(inp.bits["x"])
+    stream = torch.cuda.current_stream()
+    rows, experts, times, lines = [], [], [], []
+    for name, spec0 in (("vote16", WORKLOADS["des_vote_b025"]), ("vote32", WORKLOADS["des_vote_b050"]),
+                        ("seq", WORKLOADS["des_seq"])):
+        for n in (8, 16, 32, 64):
+            spec = spec0.replace(S=n)
+            desc = moe.desc_from_spec(spec)
+            ws = moe.workspace(desc, device=dev)
+            rb = moe.alloc_routing(desc, device=dev)
+            x = x_all[:n].contiguous()
+            y = torch.empty_like(x)
+
+            def call(i):
+                moe.moe_layer_forward(desc, x, copies[i % 4][1], None, None, rb.struct, None, None, y, ws,
+                                      stream=stream.cuda_stream)
+
+            for i in range(args.warmup):
+                call(i)
+            torch.cuda.synchronize()
+            moe.moe_profile_begin()
+            for i in range(args.steps):
+                call(i)
+            prof = moe.moe_profile_end()
+            torch.cuda.synchronize()
+            t_us = sum(prof[k][0] * 1e3 / prof[k][1] for k in ("stream_up", "stream_down") if k in prof)
+            layer_us = sum(v[0] * 1e3 / v[1] for v in prof.values())
+            counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
+            r, e = int(counts.sum()), int(np.count_nonzero(counts))
+            rows.append(r)
+            experts.append(e)
+            times.append(t_us)
+            line = {"block": name, "tokens": n, "rows": r, "experts": e,
+                    "weight_bytes": e * 3 * spec.d * spec.f * 2, "stream_us": round(t_us, 2),
+                    "kernels_us": round(layer_us, 2)}
+            lines.append(line)
+            print(json.dumps(line), flush=True)
+    A = np.stack([np.asarray(rows, float), np.asarray(experts, float), np.ones(len(rows))], axis=1)
+    coef, *_ = np.linalg.lstsq(A, np.asarray(times), rcond=None)
+    pred = A @ coef
+    d, f = base.d, base.f
+    bytes_per_expert = 3 * d * f * 2
+    print(json.dumps({"fit": "stream_us = a*rows + b*experts + c0", "a_us_per_row": round(float(coef[0]), 4),
+                      "b_us_per_expert": round(float(coef[1]), 4), "c0_us": round(float(coef[2]), 3),
+                      "max_abs_residual_us": round(float(np.abs(pred - np.asarray(times)).max()), 3),
+                      "bytes_per_expert": bytes_per_expert,
+                      "b_as_bandwidth_GBps": round(bytes_per_expert / (float(coef[1]) * 1e-6) / 1e9, 1)}),
+          flush=True)
 
 
 def sha256_of(path):
@@ -99,6 +180,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.des_fit:
+        des_fit(args)
         return
 
     import numpy as np

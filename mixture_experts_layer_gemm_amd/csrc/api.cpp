@@ -361,8 +361,13 @@ moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const voi
     if (p.streaming) {
       const int max_active = (int)std::min<int64_t>(
           {(int64_t)d->E_heavy, p.R_max, d->mode == MOE_DES_VOTE ? (int64_t)d->m_core : (int64_t)d->E_heavy});
-      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_UP, d->act, u, max_active, st), d, st));
-      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_DOWN, d->act, v, max_active, st), d, st));
+      // Token rows per streaming pass: 64 when an expert can have more than 32 rows (a token takes an
+      // expert at most once, so at most S) and the average active expert has more than 24; else 32.
+      // A pass streams the expert's weights once; the wider pass costs more token-row loads.
+      const int64_t rows_ub = std::min<int64_t>(p.R_max, d->mode == MOE_EXPERT_CHOICE ? (int64_t)p.C : (int64_t)d->S);
+      const int pass_rows = (rows_ub > 32 && p.R_max > 24 * (int64_t)max_active) ? 64 : 32;
+      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_UP, d->act, u, max_active, pass_rows, st), d, st));
+      MOE_TRY(after_launch(launch_stream_gemm(d->dtype, GEMM_DOWN, d->act, v, max_active, pass_rows, st), d, st));
     } else {
       up[nup] = u;
       dn[nup] = v;

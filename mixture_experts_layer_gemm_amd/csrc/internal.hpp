@@ -140,8 +140,10 @@ hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* 
 bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K);
 
 // Weight-streaming grouped GEMM for few rows per expert; grid.y = max_active bounds the number
-// of experts with rows (offsets-based problems only).
-hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, hipStream_t st);
+// of experts with rows (offsets-based problems only); pass_rows (32 or 64) is the number of an
+// expert's rows that one pass over its weights serves.
+hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, int pass_rows,
+                              hipStream_t st);
 bool stream_gemm_supported(int dtype, int kind, int act, int N, int K);
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);

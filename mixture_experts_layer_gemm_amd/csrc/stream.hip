@@ -154,10 +154,12 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
 // Ring streaming (bf16). A workgroup of 4 waves owns 64 weight rows (64 more gate rows with SwiGLU)
 // of one active expert; wave w takes the K stages w, w + 4, w + 8, ... (one MFMA K step, 64 bytes
 // of every row, per stage), so the four waves read neighbouring 64-byte pieces of each row at the
-// same time. Each wave streams its stages, weight rows and the 32 token rows of the pass alike,
-// through a private ring of kRingSlots LDS slots with direct global->LDS loads, kRingSlots - 1
-// stages in flight while one is multiplied: no barrier inside the loop and no register staging.
-// The four partial sums are added in LDS in wave order at the end.
+// same time. Each wave streams its stages, weight rows and the 16 * GRP token rows of the pass
+// alike, through a private ring of kRingSlots LDS slots with direct global->LDS loads,
+// kRingSlots - 1 stages in flight while one is multiplied: no barrier inside the loop and no
+// register staging. The four partial sums are added in LDS in wave order at the end. GRP (2 or 4
+// groups of 16 token rows per pass) comes from the host: an expert with more rows than a pass
+// serves streams its weights once per pass.
 constexpr int kRingRows = 64;    // weight rows per workgroup (x 2 with SwiGLU)
 constexpr int kRingSlots = 3;    // stages per wave ring
 constexpr int kRingRowB = 64;    // bytes of one row per stage
@@ -175,21 +177,22 @@ __device__ __forceinline__ void gload_lds16_va(const void* addr, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <int KIND, int ACT>
+template <int KIND, int ACT, int GRP>
 __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   using T = bf16_t;
   constexpr int EPC = Elem<T>::kPer16B;
   constexpr int BK = kRingRowB / (int)sizeof(T);               // K elements per stage
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
   constexpr int RW = SWIGLU ? 2 * kRingRows : kRingRows;       // weight rows per stage
-  constexpr int SLOT = (RW + 32) * kRingRowB;                  // + 32 token rows
+  constexpr int TR = 16 * GRP;                                  // token rows per pass
+  constexpr int SLOT = (RW + TR) * kRingRowB;
   constexpr int LPS = RW / 16;                                  // weight loads per stage
-  constexpr int PER = LPS + 2;                                  // loads per stage
+  constexpr int PER = LPS + GRP;                                // loads per stage
   constexpr int NT = kRingRows / 16;                            // 16-column subtiles (= waves)
   constexpr int NB = SWIGLU ? 2 * NT : NT;                      // weight fragments per stage
   constexpr int D = kRingSlots;
   static_assert(NT == 4, "one subtile per wave in the epilogue");
-  static_assert(4 * 2 * NB * 64 * 16 <= 4 * D * SLOT, "reduction fits in the ring");
+  static_assert(4 * GRP * NB * 64 * 16 <= 4 * D * SLOT, "reduction fits in the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][D][SLOT];
   const GemmProblem& P = la_p;
   const int e = __builtin_amdgcn_readfirstlane(locate_active(P, blockIdx.y));
@@ -214,10 +217,10 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   auto swz = [](int row, int chunk) { return row * kRingRowB + ((chunk ^ ((row >> 2) & 3)) << 4); };
   const T* A = (const T*)P.A;
 
-  for (int t0 = 0; t0 < cnt; t0 += 32) {
-    const T* xr[2];   // this lane's token row (clamped to the expert's rows) and chunk, per group
+  for (int t0 = 0; t0 < cnt; t0 += TR) {
+    const T* xr[GRP];   // this lane's token row (clamped to the expert's rows) and chunk, per group
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < GRP; ++g) {
       const int r = beg + min(t0 + g * 16 + rr, cnt - 1);
       const int src = P.a_rows ? P.a_rows[r] : r;
       xr[g] = A + (size_t)src * P.lda + cc * EPC + (size_t)wave * BK;
@@ -232,23 +235,23 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
         gload_lds16(base, lane_off, dst + i * 16 * kRingRowB);
       }
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < GRP; ++g)
         gload_lds16_va(xr[g] + (size_t)s * 4 * BK, dst + (RW + g * 16) * kRingRowB);
     };
-    floatx4_t acc[2][NB];
+    floatx4_t acc[GRP][NB];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < GRP; ++g)
 #pragma unroll
       for (int i = 0; i < NB; ++i) acc[g][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     auto compute = [&](int s) {
       const uint8_t* sp = myring + (s % D) * SLOT;
-      uint4 bf[NB], xv[2];
+      uint4 bf[NB], xv[GRP];
 #pragma unroll
       for (int i = 0; i < NB; ++i) bf[i] = *reinterpret_cast<const uint4*>(sp + swz(i * 16 + fr, fg));
 #pragma unroll
-      for (int g = 0; g < 2; ++g) xv[g] = *reinterpret_cast<const uint4*>(sp + swz(RW + g * 16 + fr, fg));
+      for (int g = 0; g < GRP; ++g) xv[g] = *reinterpret_cast<const uint4*>(sp + swz(RW + g * 16 + fr, fg));
 #pragma unroll
-      for (int g = 0; g < 2; ++g)
+      for (int g = 0; g < GRP; ++g)
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[g][i] = mfma16(bf[i], xv[g], acc[g][i], T());
     };
@@ -273,21 +276,21 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
     __syncthreads();
     floatx4_t* red = reinterpret_cast<floatx4_t*>(&ring[0][0][0]);   // [wave][g][NB][64]
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < GRP; ++g)
 #pragma unroll
-      for (int i = 0; i < NB; ++i) red[((wave * 2 + g) * NB + i) * 64 + lane] = acc[g][i];
+      for (int i = 0; i < NB; ++i) red[((wave * GRP + g) * NB + i) * 64 + lane] = acc[g][i];
     __syncthreads();
     const int nt = wave;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < GRP; ++g) {
       floatx4_t u = floatx4_t{0.f, 0.f, 0.f, 0.f}, gt = u;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const floatx4_t a = red[((w * 2 + g) * NB + nt) * 64 + lane];
+        const floatx4_t a = red[((w * GRP + g) * NB + nt) * 64 + lane];
 #pragma unroll
         for (int t = 0; t < 4; ++t) u[t] += a[t];
         if (SWIGLU) {
-          const floatx4_t b = red[((w * 2 + g) * NB + NT + nt) * 64 + lane];
+          const floatx4_t b = red[((w * GRP + g) * NB + NT + nt) * 64 + lane];
 #pragma unroll
           for (int t = 0; t < 4; ++t) gt[t] += b[t];
         }
@@ -318,10 +321,15 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
 }
 
 template <int KIND, int ACT>
-static void ring_t(const GemmProblem& la, int max_active, hipStream_t st) {
+static void ring_t(const GemmProblem& la, int max_active, int pass_rows, hipStream_t st) {
   const dim3 grid(la.N / kRingRows, max_active);
-  auto kfn = k_stream_ring<KIND, ACT>;
-  MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+  if (pass_rows > 32) {
+    auto kfn = k_stream_ring<KIND, ACT, 4>;
+    MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+  } else {
+    auto kfn = k_stream_ring<KIND, ACT, 2>;
+    MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+  }
 }
 
 bool stream_gemm_supported(int dtype, int kind, int act, int N, int K) {
@@ -358,13 +366,14 @@ static void launch_stream_t(const GemmProblem& la, int kind, int act, int max_ac
   else stream_t<T, GEMM_UP, ACT_GELU>(la, max_active, st);
 }
 
-hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, hipStream_t st) {
+hipError_t launch_stream_gemm(int dtype, int kind, int act, const GemmProblem& p, int max_active, int pass_rows,
+                              hipStream_t st) {
   if (max_active <= 0 || !p.offsets) return hipSuccess;
   if (stream_ring_supported(dtype, p.N, p.K) && p.k_seg == p.K) {
-    if (kind == GEMM_DOWN) ring_t<GEMM_DOWN, ACT_GELU>(p, max_active, st);
-    else if (act == ACT_SWIGLU) ring_t<GEMM_UP, ACT_SWIGLU>(p, max_active, st);
-    else if (act == ACT_GELU_TANH) ring_t<GEMM_UP, ACT_GELU_TANH>(p, max_active, st);
-    else ring_t<GEMM_UP, ACT_GELU>(p, max_active, st);
+    if (kind == GEMM_DOWN) ring_t<GEMM_DOWN, ACT_GELU>(p, max_active, pass_rows, st);
+    else if (act == ACT_SWIGLU) ring_t<GEMM_UP, ACT_SWIGLU>(p, max_active, pass_rows, st);
+    else if (act == ACT_GELU_TANH) ring_t<GEMM_UP, ACT_GELU_TANH>(p, max_active, pass_rows, st);
+    else ring_t<GEMM_UP, ACT_GELU>(p, max_active, pass_rows, st);
     return hipGetLastError();
   }
   if (dtype == 0) launch_stream_t<bf16_t>(p, kind, act, max_active, st);

@@ -74,6 +74,9 @@ WORKLOADS: dict[str, LayerSpec] = {
                                mode="des", k=8, renorm=True, vote_k=8, m_core=16),
     "des_vote_b050": LayerSpec("des_vote_b050", S=32, d=2048, f=1024, E_heavy=64, act="swiglu",
                                mode="des", k=8, renorm=True, vote_k=8, m_core=32),
+    # DES-Seq on the same block: every token keeps its own top-8; the experts loaded are the union.
+    "des_seq": LayerSpec("des_seq", S=32, d=2048, f=1024, E_heavy=64, act="swiglu", mode="tc", k=8,
+                         renorm=True),
     # MMOE MoE++: 64 x 256 tokens, d=1152, 16 heavy GELU experts + identity/zero/constant + 1 shared,
     # top-2 over 19 with gate residual, 4 stacked layers.
     "mmoe": LayerSpec("mmoe", S=16384, d=1152, f=4608, E_heavy=16, n_identity=1, n_zero=1, n_const=1,

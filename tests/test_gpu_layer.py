@@ -91,6 +91,27 @@ def test_des_layer_full_size(name):
     _layer_case(spec, flags=moe.MOE_F_FORCE_TILED)
 
 
+def test_des_seq_layer_full_size():
+    """DES-Seq ("Dynamic Expert Sharing", 2.3): each token of the block keeps its own top-8 and the
+    experts streamed are their union. Layer parity, and the streamed set equals the oracle's
+    DES-Seq core of the (reconciled) routing."""
+    spec = WORKLOADS["des_seq"]
+    inp, rt, _ = _layer_case(spec)
+    inp2 = gen_layer_inputs(spec, seed=0)
+    x = dev_tensor(inp2.x, inp2.bits.get("x"), spec.dtype)
+    _, logits, rb = run_layer(spec, x, upload_layer(inp2))
+    counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
+    active = np.flatnonzero(counts > 0)
+    L64 = orc.router_logits(inp2.x, inp2.w_router[0])
+    rt2 = _oracle_rt(spec, L64, rb)
+    assert np.array_equal(active, np.unique(rt2["idx"]))
+    # without near-ties the reconciled routing is the oracle's own, and so is the union
+    core = orc.des_seq_core(L64, spec.k)
+    if np.array_equal(rt2["idx"], orc.route(spec, L=L64)["idx"]):
+        assert np.array_equal(active, core)
+    assert counts.sum() == spec.S * spec.k
+
+
 @pytest.mark.parametrize("d,f,act,S", [
     (256, 256, "swiglu", 32),       # up: 2 stages per wave (the ring's minimum); down: 2
     (384, 640, "swiglu", 40),       # odd stage counts (3 and 5)
