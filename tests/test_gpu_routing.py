@@ -62,6 +62,10 @@ TC_CASES = [
     (64, 5, 0, 0, 0, 5),
     (300, 1, 0, 0, 0, 1),
     (5000, 0, 1, 1, 1, 2),
+    # one-workgroup kernel with a wave per token: 1, 2 and 4 experts per lane
+    (100, 64, 0, 0, 0, 8),
+    (60, 100, 0, 0, 0, 6),
+    (40, 200, 0, 0, 0, 16),
 ]
 
 
@@ -153,6 +157,9 @@ DES_CASES = [
     (6, 10, 3, 4, 2),
     (100, 19, 4, 3, 8),
     (257, 128, 16, 40, 16),
+    # one-workgroup kernel with 2 and 4 experts per lane
+    (60, 100, 6, 20, 6),
+    (50, 150, 8, 40, 8),
 ]
 
 
