@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--workload", default="dit_moe_xl", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
+    ap.add_argument("--dice-steps", action="store_true",
+                    help="DICE denoising-step loop: reuse fraction and time per step under three policies")
     ap.add_argument("--des-fit", action="store_true",
                     help="fit the DES per-expert latency model f(c) = a*c + b on the streaming kernels")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -151,6 +153,86 @@ def des_fit(args):
           flush=True)
 
 
+def dice_steps(args):
+    """The DICE step loop on one GPU ("DICE: Staleness-Centric Optimizations for Parallel Diffusion MoE
+    Inference", 关键设计). A stack of 4 DiT-MoE-XL-shaped MoE layers (residual stream) runs T = 10
+    denoising steps whose input drifts a little each step. Per layer and step, tokens whose top
+    routing score is below tau reuse the layer's cached routed output (conditional communication,
+    here: skipped expert rows); every `stride`-th step refreshes all tokens; with selective sync the
+    deeper half of the layers never reuses. Policies: no reuse; reuse in every layer; DICE (shallow
+    half reuses, deep half synchronous). Prints one JSON line per policy: time per step (HIP events
+    over the whole loop), the fraction of (token, layer) pairs reused, and the speed-up over no reuse."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_gemm_amd as moe
+    from synth import WORKLOADS, gen_layer_inputs, gen_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L, T, stride, tau = 4, 10, 4, 0.3
+    spec = WORKLOADS["dit_moe_xl"].replace(n_layers=L)
+    inp = gen_layer_inputs(spec, seed=0)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ws_l = []
+    for layer in range(L):
+        t = {"w_router": up(inp.bits[f"w_router.{layer}"])}
+        for n in ("w1", "w3", "w2", "s_w1", "s_w3", "s_w2"):
+            t[n] = up(inp.bits[f"{n}.{layer}"])
+        ws_l.append((t, moe.weights_struct(t)))
+    x0 = up(inp.bits["x"])
+    rng = np.random.default_rng(3)
+    drift = []
+    for _ in range(T):   # the step-to-step change of the latent tokens
+        v, b = gen_tensor(rng, (spec.S, spec.d), 0.02, "bf16")
+        drift.append(up(b))
+    d_fresh = moe.desc_from_spec(spec.replace(reuse_tau=0.0))
+    d_reuse = moe.desc_from_spec(spec.replace(reuse_tau=tau))
+    ws = moe.workspace(d_reuse, device=dev)
+    rbs = [moe.alloc_routing(d_reuse, device=dev) for _ in range(L)]
+    stream = torch.cuda.current_stream()
+    caches = [torch.zeros((spec.S, spec.d), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    hs = [torch.empty_like(x0) for _ in range(L)]
+    xt = torch.empty_like(x0)
+    results = {}
+    for policy in ("none", "all", "dice"):
+        def run(count):
+            reused = 0
+            xt.copy_(x0)
+            for t in range(T):
+                xt.add_(drift[t])
+                h = xt
+                for layer in range(L):
+                    use = policy == "all" or (policy == "dice" and layer < L // 2)
+                    fresh = (not use) or t % stride == 0
+                    desc = d_fresh if fresh else d_reuse
+                    moe.moe_layer_forward(desc, h, ws_l[layer][1], None, None, rbs[layer].struct, caches[layer], h,
+                                          hs[layer], ws, stream=stream.cuda_stream)
+                    if count and not fresh:
+                        reused += int(rbs[layer]["reuse"].sum().item())
+                    h = hs[layer]
+            return reused
+
+        run(False)   # warm-up (also fills the caches)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        run(False)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / T
+        reused = run(True)
+        frac = reused / float(T * L * spec.S)
+        results[policy] = ms
+        line = {"dice_policy": policy, "layers": L, "steps": T, "stride": stride, "tau": tau, "tokens": spec.S,
+                "ms_per_step": round(ms, 4), "reused_fraction": round(frac, 4),
+                "speedup_vs_no_reuse": round(results["none"] / ms, 3)}
+        print(json.dumps(line), flush=True)
+
+
 def sha256_of(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -183,6 +265,9 @@ def main():
         return
     if args.des_fit:
         des_fit(args)
+        return
+    if args.dice_steps:
+        dice_steps(args)
         return
 
     import numpy as np
