@@ -92,25 +92,36 @@ enum { ACT_GELU = 0, ACT_GELU_TANH = 1, ACT_SWIGLU = 2 };
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 
-// erf by the approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, formula
-// 7.1.28 (|error| <= 3e-7): erf(x) = 1 - (1 + a1 x + ... + a6 x^6)^-16 for x >= 0, odd extension
-// for x < 0. One reciprocal and no exponential; in fp32 the GELU built on it is within 1e-6 of
-// the exact function, far below the bf16 rounding of the stored activation.
-__device__ __forceinline__ float erf_as(float x) {
-  const float ax = fabsf(x);
-  float p = fmaf(0.0000430638f, ax, 0.0002765672f);
-  p = fmaf(p, ax, 0.0001520143f);
-  p = fmaf(p, ax, 0.0092705272f);
-  p = fmaf(p, ax, 0.0422820123f);
-  p = fmaf(p, ax, 0.0705230784f);
-  p = fmaf(p, ax, 1.0f);
-  p = p * p;
-  p = p * p;
-  p = p * p;
-  p = p * p;   // (...)^16; overflows to inf for large x, whose reciprocal is 0
-  return copysignf(1.0f - fast_rcp(p), x);
+// erf GELU, z * Phi(z), written as max(z, 0) - |z| * Q(|z|) with Q(u) = 1 - Phi(u) = erfc(u / sqrt 2) / 2
+// (for z >= 0 that is z - z Q; for z < 0 it is z Phi(z) = z Q(|z|)). erfc comes from the
+// approximation of Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.28
+// (|error| <= 3e-7 for x >= 0): erfc(x) = (1 + a1 x + ... + a6 x^6)^-16, so Q(u) = q(u)^-16 with
+// q(u) = 2^(1/16) (1 + a1 u/sqrt2 + ... + a6 (u/sqrt2)^6). The coefficients of q are those of the
+// formula rescaled by 2^(1/16) and powers of 1/sqrt 2 (exact in double, rounded once to float).
+// Twelve VALU operations and one reciprocal; |error| <= 8e-7 over all z.
+__device__ __forceinline__ float gelu_erf(float z) {
+  constexpr double c = 1.0442737824274138;   // 2^(1/16)
+  constexpr double s = 0.70710678118654752;  // 1/sqrt(2)
+  constexpr float b0 = (float)c;
+  constexpr float b1 = (float)(c * 0.0705230784 * s);
+  constexpr float b2 = (float)(c * 0.0422820123 * s * s);
+  constexpr float b3 = (float)(c * 0.0092705272 * s * s * s);
+  constexpr float b4 = (float)(c * 0.0001520143 * s * s * s * s);
+  constexpr float b5 = (float)(c * 0.0002765672 * s * s * s * s * s);
+  constexpr float b6 = (float)(c * 0.0000430638 * s * s * s * s * s * s);
+  const float u = fabsf(z);
+  float q = fmaf(b6, u, b5);
+  q = fmaf(q, u, b4);
+  q = fmaf(q, u, b3);
+  q = fmaf(q, u, b2);
+  q = fmaf(q, u, b1);
+  q = fmaf(q, u, b0);
+  q = q * q;
+  q = q * q;
+  q = q * q;
+  q = q * q;   // q^16; overflows to inf for large |z|, whose reciprocal is 0
+  return fmaf(-u, fast_rcp(q), fmaxf(z, 0.0f));
 }
-__device__ __forceinline__ float gelu_erf(float z) { return 0.5f * z * (1.0f + erf_as(z * 0.70710678118654752f)); }
 // tanh form: 0.5 z (1 + tanh(u)) = z - z / (1 + e^{2u}), u = sqrt(2/pi) (z + 0.044715 z^3)
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float u = 0.79788456080286536f * fmaf(0.044715f * z, z * z, z);
