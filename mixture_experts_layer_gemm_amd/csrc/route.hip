@@ -506,9 +506,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
 // Small calls (a DES decode block, a tiny batch): the whole routing of token choice or DES-Vote and
 // the counting-sort dispatch in one workgroup: one launch instead of four. The selections are the
 // same as in k_route_topk / k_route_des (the same keys, order and tie rule; for a token spread over
-// a whole wave, wave_topk takes each maximum with a DPP reduction instead of shuffles); votes are
-// summed in the same order, and rows come out in the same (expert, token, slot) order as the three
-// permute kernels. Barriers here wait for LDS only (lds_barrier).
+// a whole wave, wave_topk finds them by a radix select over ballots instead of shuffles; the core
+// and the re-route inside it rank experts by comparison counts); votes are summed in the same
+// order, and rows come out in the same (expert, token, slot) order as the three permute kernels.
+// Barriers here wait for LDS only (lds_barrier).
 constexpr int kSmallThreads = 1024;
 constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallMaxSE = 8192;     // S * E_r: keys and probabilities kept in LDS

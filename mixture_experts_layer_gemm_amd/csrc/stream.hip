@@ -1,18 +1,22 @@
-// Weight-streaming grouped GEMM for experts that receive only a few rows.
+// Weight-streaming grouped GEMMs for experts that receive only a few rows.
 //
 // In a DES decode block each active expert serves ~N*k/M_core rows (8-32), so its time is the
 // fetch of its weights from HBM: "Dynamic Expert Sharing: Decoupling Memory from Parallelism in
 // Mixture-of-Experts Diffusion LLMs", 2.1 (per-expert latency a*c + b, b the HBM weight fetch;
-// the block latency is dominated by b times the number of distinct experts loaded). This kernel
-// reads every weight byte of an active expert exactly once and keeps the MFMA work beside it.
+// the block latency is dominated by b times the number of distinct experts loaded). These kernels
+// read every weight byte of an active expert once per pass over its rows and keep the MFMA work
+// beside the loads. Experts with no rows are skipped, so bytes = (active experts) x (weight bytes
+// per expert) per pass.
 //
-// Layout: workgroup (x = slice of 16 * G columns, y = active-expert slot) of G * SL waves. Wave w
-// owns 16 output columns (16 weight rows; 32 for SwiGLU gate+up): column group w % G, K slice
-// w / G. The slices take blocks of 4 MFMA steps (256 bytes of each row) in turn; each load
-// instruction reads 64 contiguous bytes of each of 16 rows. Weight rows are MFMA operand P,
-// streamed from HBM with non-temporal loads; the expert's token rows (operand Q, gathered through
+// k_stream_ring (bf16, the usual path; described at its definition) streams weight and token rows
+// through per-wave LDS rings with direct global->LDS loads. k_stream_gemm covers fp32 and the
+// shapes the ring does not take:
+// workgroup (x = slice of 16 * G columns, y = active-expert slot) of G * SL waves. Wave w owns 16
+// output columns (16 weight rows; 32 for SwiGLU gate+up): column group w % G, K slice w / G. The
+// slices take blocks of 4 MFMA steps (256 bytes of each row) in turn; each load instruction reads
+// 64 contiguous bytes of each of 16 rows. Weight rows are MFMA operand P, streamed from HBM with
+// non-temporal loads into registers; the expert's token rows (operand Q, gathered through
 // row_token) come from L2, 32 rows per pass. The K slices are added in LDS in slice order.
-// Experts with no rows are skipped, so bytes = (active experts) x (weight bytes per expert).
 #include "common.hpp"
 #include "internal.hpp"
 
