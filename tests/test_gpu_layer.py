@@ -112,15 +112,17 @@ def test_des_seq_layer_full_size():
     assert counts.sum() == spec.S * spec.k
 
 
-@pytest.mark.parametrize("d,f,act,S", [
-    (256, 256, "swiglu", 32),       # up: 2 stages per wave (the ring's minimum); down: 2
-    (384, 640, "swiglu", 40),       # odd stage counts (3 and 5)
-    (256, 128, "gelu", 32),         # down K=128 is below the ring's minimum: register streaming
-    (512, 256, "gelu_tanh", 24),
-    (256, 384, "gelu", 200),        # many rows per expert: several 32-row passes
+@pytest.mark.parametrize("d,f,act,S,m_core", [
+    (256, 256, "swiglu", 32, 16),     # up: 2 stages per wave (the ring's minimum); down: 2
+    (384, 640, "swiglu", 40, 16),     # odd stage counts (3 and 5)
+    (256, 128, "gelu", 32, 16),       # down K=128 is below the ring's minimum: register streaming
+    (512, 256, "gelu_tanh", 24, 16),
+    (256, 384, "gelu", 200, 16),      # many rows per expert: several 32-row passes
+    (2048, 256, "gelu", 32, 16),      # wide down projection (32 x 16 workgroups)
+    (1024, 2048, "gelu", 100, 32),    # 32 active experts, 64-row passes
 ])
-def test_stream_shapes(d, f, act, S):
-    spec = WORKLOADS["des_vote_b025"].replace(S=S, d=d, f=f, act=act)
+def test_stream_shapes(d, f, act, S, m_core):
+    spec = WORKLOADS["des_vote_b025"].replace(S=S, d=d, f=f, act=act, m_core=m_core)
     _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
 
 
