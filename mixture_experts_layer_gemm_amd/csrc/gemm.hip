@@ -10,12 +10,16 @@
 //
 // Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 192, 256}; each wave
 // owns 128 token rows x BN/2 weight rows, the 2 x 2 split with the fewest LDS reads per MFMA):
-//   * K advances one MFMA K step (64 bytes of every tile row) per stage. Stages go through a ring
-//     of five LDS slots, filled by direct global->LDS loads (no staging registers): four stages
-//     are in flight while one feeds the MFMAs, which hides L2-miss latency; one barrier per stage.
-//   * The loads of a stage and the LDS fragment reads of the next one are spread between the
+//   * K advances in blocks of two MFMA K steps: 128 bytes of every tile row, one whole cache line,
+//     so every 16-byte-per-lane load instruction reads 8 full lines (reading 64-byte halves made
+//     twice the L2 requests for the same bytes, and the L2 request rate was the limit).
+//   * The A block (256 token rows) and the B block (BN weight rows) of a K block each fill one
+//     32 KB unit of a five-unit LDS ring, by direct global->LDS loads (no staging registers). One
+//     operand (L) is loaded two blocks ahead, the other (S) one block ahead; the up projections
+//     give the weights the long lead, the down projections the tokens. One barrier per block.
+//   * The loads of a block and the LDS fragment reads of the next step are spread between the
 //     MFMAs of the current one (sched_group_barrier regions), so issue never stalls on a full queue.
-//   * LDS rows are 64 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 2) & 3), so the 16-byte
+//   * LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), so the 16-byte
 //     fragment reads of 16 consecutive rows cover all banks once.
 //   * Weights are MFMA operand P and tokens operand Q, so each lane ends with 4 consecutive output
 //     columns of one row: 8-byte (bf16) / 16-byte (fp32) stores.
@@ -23,7 +27,7 @@
 //   * Tile order: workgroup b runs on XCD b % 8; tiles are renumbered so each XCD owns a
 //     contiguous range, swept as 8 m-tiles x all n-tiles, which keeps an expert's weight panels and
 //     token panels in one XCD's L2.
-//   * The expert of an m-tile comes from a wave-wide scan of ceil(count_e / 256) over experts.
+//   * The expert of an m-tile comes from a scalar scan of ceil(count_e / 256) over experts.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -34,8 +38,10 @@
 namespace moe {
 
 constexpr int kBM = 256;
-constexpr int kRowB = 64;           // bytes of one tile row per stage (one MFMA K-step)
-constexpr int kStages = 5;          // LDS ring: four stages in flight while one is consumed
+constexpr int kRowB = 128;          // bytes of one tile row per LDS unit: one cache line, two MFMA K steps
+constexpr int kStepB = 64;          // bytes of one tile row per MFMA K step
+constexpr int kUnits = 5;           // LDS ring of 32 KB units; the A and B units of the K blocks alternate
+constexpr int kUnitB = 32768;
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
 constexpr int kWaves = 4;           // 2 x 2 wave grid, one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
@@ -47,9 +53,10 @@ struct GemmLaunch {
   int32_t slots0, slots1;   // workgroups per XCD reserved for each problem (from upper bounds)
 };
 
-// 16-byte chunk c (0..3) of tile row r sits at slot c ^ ((r >> 2) & 3): the 16-byte fragment reads
-// of 16 consecutive rows then cover all 64 banks once.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// 16-byte chunk c (0..7) of tile row r sits at slot c ^ ((r >> 1) & 7): the 16-byte fragment reads
+// of 16 consecutive rows (one chunk each) then cover all 64 banks once (the even rows fill one half
+// of the 256-byte bank cycle, the odd rows the other).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // m-tiles of a problem: groups in order, ceil(rows_g / 256) tiles each. The group offsets are read
 // with scalar loads (constant address space: the kernel never writes them), so finding a tile's
@@ -104,7 +111,7 @@ __device__ __forceinline__ bool mtile_locate(const GemmProblem& P, int mt, int& 
 // MFMAs of MFMAs [M0, M1) (loads bound the regions).
 template <int NM, int NF, int LPS, int MPC>
 struct step_sched {
-  static constexpr int load_pos(int d) { return d < 0 ? 0 : (d * NM) / LPS; }
+  static constexpr int load_pos(int d) { return d < 0 || LPS == 0 ? 0 : (d * NM) / LPS; }
   static constexpr int load_at(int m) {
     for (int d = 0; d < LPS; ++d)
       if (load_pos(d) == m) return d;
@@ -141,25 +148,23 @@ struct step_sched {
 template <typename T, int KIND, int ACT, int BN>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int EPC = Elem<T>::kPer16B;        // elements per 16-byte chunk
-  constexpr int BK = kRowB / sizeof(T);        // K elements per stage
+  constexpr int BK = kStepB / sizeof(T);       // K elements per MFMA step
+  constexpr int BU = 2 * BK;                   // K elements per unit (one K block)
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
   constexpr int NI = BN / 32;                  // 16-row n-subtiles per wave (wave covers BN/2 B rows)
   constexpr int MJ = 8;                        // 16-row m-subtiles per wave (wave covers 128 rows)
   constexpr int NF = MJ + NI;                  // fragments per K step
-  constexpr int A_BYTES = kBM * kRowB;
-  constexpr int B_BYTES = BN * kRowB;
-  constexpr int STAGE = A_BYTES + B_BYTES;
-  constexpr int A_LD = kBM / (kRowsPerLoad * kWaves);   // wave load instructions per stage
-  constexpr int B_LD = BN / (kRowsPerLoad * kWaves);
-  constexpr int LPS = A_LD + B_LD;                       // loads per wave per stage
-  // One array per ring stage: with the K loop unrolled every LDS access names its stage at compile
-  // time. Five 32 KB slots are all of LDS; nothing else in the kernel uses LDS.
-  static_assert(kStages == 5, "the ring below is written for five stages");
-  __shared__ __attribute__((aligned(16))) uint8_t smem0[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem1[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem2[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem3[STAGE];
-  __shared__ __attribute__((aligned(16))) uint8_t smem4[STAGE];
+  constexpr int A_LD = kBM / (kRowsPerLoad * kWaves);   // wave load instructions per A unit
+  constexpr int B_LD = BN / (kRowsPerLoad * kWaves);    // per B unit
+  static_assert(kBM * kRowB <= kUnitB && BN * kRowB <= kUnitB, "a unit holds one K block of A or of B");
+  // One array per ring unit: with the K loop unrolled every LDS access names its unit at compile
+  // time. Five 32 KB units are all of LDS; nothing else in the kernel uses LDS.
+  static_assert(kUnits == 5, "the ring below is written for five units");
+  __shared__ __attribute__((aligned(16))) uint8_t smem0[kUnitB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem1[kUnitB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem2[kUnitB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem3[kUnitB];
+  __shared__ __attribute__((aligned(16))) uint8_t smem4[kUnitB];
 
   // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
   // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
@@ -190,9 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- per-lane source offsets. Load instruction i of wave w fills tile rows
-  // i*16*kWaves + 16w .. +16; lane l writes row r = i*16*kWaves + 16w + l/4 at slot l%4, i.e. the
-  // chunk (l%4) ^ ((r >> 2) & 3) of that row.
+  // ---- per-lane source offsets. Load instruction i of wave w fills the 128-byte rows
+  // i*8*kWaves + 8w .. +8 of a unit; lane l writes row r = i*8*kWaves + 8w + l/8 at slot l%8, i.e. the
+  // chunk (l%8) ^ ((r >> 1) & 7) of that row. Eight lanes read one whole cache line.
   const T* __restrict__ Ab = (const T*)P.A;
   const T* __restrict__ Bb = (const T*)P.B + (size_t)g * P.b_gstride;
   const T* __restrict__ B3b = SWIGLU ? (const T*)P.B3 + (size_t)g * P.b_gstride : nullptr;
@@ -201,16 +206,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   bool b_gate[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int orow = row0 + min(r, rows - 1);
     const int arow = P.a_rows ? P.a_rows[orow] : orow;
     a_off[i] = (uint32_t)(((size_t)arow * P.lda + c * EPC) * sizeof(T));
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const bool gate = SWIGLU && r >= BN / 2;   // the same for the whole wave
     b_gate[i] = gate;
     // rows past N (a ragged last column tile) re-read row N-1; their columns are not stored
@@ -218,32 +223,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     b_off[i] = (uint32_t)(((size_t)brow * P.ldb + c * EPC) * sizeof(T));
   }
 
-  const int nk = P.K / BK;
-  // Source positions of the next stage to load: K offset into A, and into B (whose K axis may be
-  // split into segments of k_seg elements placed k_seg_stride apart). Stages are issued in order,
-  // one per K step; stages past the end re-load the last stage (valid memory that the load just
-  // before brought into the caches; never read).
+  const int nu = P.K / BU;   // K blocks (two MFMA steps each)
+  // Source positions of the next A and B units to load: K offset into A, and into B (whose K axis
+  // may be split into segments of k_seg elements placed k_seg_stride apart). Units of each kind are
+  // issued in order; past the end the position stays on the last block (valid memory that the load
+  // just before brought into the caches; never read).
   const int k_seg = (int)P.k_seg;
   const int64_t k_skip = P.k_seg_stride - P.k_seg;
   int64_t a_k = 0, b_k = 0;
-  int b_within = 0, issued = 0;
+  int b_within = 0, a_issued = 0, b_issued = 0;
   const uint32_t wave_off = (uint32_t)(wave * kRowsPerLoad * kRowB);
   struct Dma {
-    const T* a;
-    const T* b;
-    const T* b3;
+    const T* p;    // A, or B (W1) rows
+    const T* p3;   // SwiGLU gate rows (W3)
     uint32_t lds;
   };
-  auto next_dma = [&](uint32_t stage) -> Dma {
+  auto next_a = [&](uint32_t unit) -> Dma {
     Dma d;
-    d.a = Ab + a_k;
-    d.b = Bb + b_k;
-    d.b3 = SWIGLU ? B3b + b_k : nullptr;
-    d.lds = stage + wave_off;
-    if (++issued < nk) {   // past the end the position stays on the last stage
-      a_k += BK;
-      b_k += BK;
-      b_within += BK;
+    d.p = Ab + a_k;
+    d.p3 = nullptr;
+    d.lds = unit + wave_off;
+    if (++a_issued < nu) a_k += BU;
+    return d;
+  };
+  auto next_b = [&](uint32_t unit) -> Dma {
+    Dma d;
+    d.p = Bb + b_k;
+    d.p3 = SWIGLU ? B3b + b_k : nullptr;
+    d.lds = unit + wave_off;
+    if (++b_issued < nu) {
+      b_k += BU;
+      b_within += BU;
       if (b_within == k_seg) {
         b_within = 0;
         b_k += k_skip;
@@ -251,26 +261,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     }
     return d;
   };
-  // load instruction q (0..LPS) of a stage: A loads first, then B
-  auto dma_one = [&](const Dma& d, auto Qc) {
+  constexpr uint32_t kLoadStride = kRowsPerLoad * kWaves * kRowB;   // LDS bytes between a wave's loads
+  auto dma_a = [&](const Dma& d, auto Qc) {
     constexpr int q = decltype(Qc)::value;
-    if constexpr (q < A_LD) {
-      gload_lds16(d.a, a_off[q], d.lds + q * kRowsPerLoad * kWaves * kRowB);
-    } else {
-      constexpr int i = q - A_LD;
-      gload_lds16(b_gate[i] ? d.b3 : d.b, b_off[i], d.lds + A_BYTES + i * kRowsPerLoad * kWaves * kRowB);
-    }
+    gload_lds16(d.p, a_off[q], d.lds + q * kLoadStride);
   };
-  auto issue_all = [&](const Dma& d) {
-    dma_one(d, std::integral_constant<int, 0>{});
-    if constexpr (LPS > 1) dma_one(d, std::integral_constant<int, 1>{});
-    if constexpr (LPS > 2) dma_one(d, std::integral_constant<int, 2>{});
-    if constexpr (LPS > 3) dma_one(d, std::integral_constant<int, 3>{});
-    if constexpr (LPS > 4) dma_one(d, std::integral_constant<int, 4>{});
-    if constexpr (LPS > 5) dma_one(d, std::integral_constant<int, 5>{});
-    if constexpr (LPS > 6) dma_one(d, std::integral_constant<int, 6>{});
-    if constexpr (LPS > 7) dma_one(d, std::integral_constant<int, 7>{});
-    static_assert(LPS <= 8, "at most 8 loads per stage");
+  auto dma_b = [&](const Dma& d, auto Qc) {
+    constexpr int i = decltype(Qc)::value;
+    gload_lds16(b_gate[i] ? d.p3 : d.p, b_off[i], d.lds + i * kLoadStride);
+  };
+  auto issue_a = [&](const Dma& d) {
+    dma_a(d, std::integral_constant<int, 0>{});
+    dma_a(d, std::integral_constant<int, 1>{});
+    dma_a(d, std::integral_constant<int, 2>{});
+    dma_a(d, std::integral_constant<int, 3>{});
+    dma_a(d, std::integral_constant<int, 4>{});
+    dma_a(d, std::integral_constant<int, 5>{});
+    dma_a(d, std::integral_constant<int, 6>{});
+    dma_a(d, std::integral_constant<int, 7>{});
+    static_assert(A_LD == 8, "eight loads per A unit");
+  };
+  // The ring alternates the units of two operands: L, which is loaded two blocks ahead of its use,
+  // and S, loaded one block ahead (below). The up projections give the weights the longer lead,
+  // the down projections the tokens (measured on the dense SwiGLU up and long-K down shapes).
+  constexpr bool B_LONG = KIND == GEMM_UP;
+  constexpr int L_LD = B_LONG ? B_LD : A_LD, S_LD = B_LONG ? A_LD : B_LD;
+  auto issue_b = [&](const Dma& d) {
+    dma_b(d, std::integral_constant<int, 0>{});
+    dma_b(d, std::integral_constant<int, 1>{});
+    dma_b(d, std::integral_constant<int, 2>{});
+    dma_b(d, std::integral_constant<int, 3>{});
+    if constexpr (B_LD > 4) dma_b(d, std::integral_constant<int, 4>{});
+    if constexpr (B_LD > 5) dma_b(d, std::integral_constant<int, 5>{});
+    if constexpr (B_LD > 6) dma_b(d, std::integral_constant<int, 6>{});
+    if constexpr (B_LD > 7) dma_b(d, std::integral_constant<int, 7>{});
+    static_assert(B_LD >= 4 && B_LD <= 8, "four to eight loads per B unit");
   };
 
   // B-tile row of n-subtile i for this wave.
@@ -289,80 +314,120 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     for (int j = 0; j < MJ; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fg = lane >> 4;
-  // Fragments of one K step: f[0..MJ) token rows (operand Q), f[MJ..) weight rows (operand P).
-  auto read_frags = [&](const uint8_t* stage, uint4 (&f)[NF]) {
-#pragma unroll
-    for (int j = 0; j < MJ; ++j) f[j] = *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + j * 16 + fr, fg));
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      f[MJ + i] = *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(i) + fr, fg));
+  // Fragment q of K step s of a block: q < MJ token rows (operand Q, from the A unit ua), else
+  // weight rows (operand P, from the B unit ub); 16-byte chunk 4s + fg of the 128-byte row.
+  auto read_frag = [&](const uint8_t* ua, const uint8_t* ub, auto Sc, auto Qc) -> uint4 {
+    constexpr int st = decltype(Sc)::value, q = decltype(Qc)::value;
+    if constexpr (q < MJ) return *reinterpret_cast<const uint4*>(ua + swz(wm * 128 + q * 16 + fr, st * 4 + fg));
+    else return *reinterpret_cast<const uint4*>(ub + swz(brow_of(q - MJ) + fr, st * 4 + fg));
+  };
+  auto read_all = [&](auto self, auto Qc, const uint8_t* ua, const uint8_t* ub, uint4 (&f)[NF]) -> void {
+    constexpr int q = decltype(Qc)::value;
+    if constexpr (q < NF) {
+      f[q] = read_frag(ua, ub, std::integral_constant<int, 0>{}, Qc);
+      self(self, std::integral_constant<int, q + 1>{}, ua, ub, f);
+    }
   };
 
-  // One K step t, after the barrier: MFMAs on the fragments of stage t (cur) with, spread between
-  // them, the LDS reads of stage t + 1 (into nxt) and the loads of stage t + 5 (into the LDS slot
-  // of stage t, free once every wave has passed the barrier). Issued as blocks, the LDS reads would
-  // fill the LDS queue and the loads the memory queue, stalling the wave before its MFMAs (issue is
-  // in order). Loads are inline assembly, which the scheduler does not move, so the step is a chain
-  // of regions separated by loads, each with its own sched_group_barrier pattern. The body is
-  // generated by compile-time recursion so that every accumulator index is a constant.
+  // One K step: MFMAs on the fragments in registers (cur) with, spread between them, the LDS reads
+  // of the next step's fragments (into nxt) and, on the second step of a block, the loads of two
+  // units. Issued as blocks, the LDS reads would fill the LDS queue and the loads the memory queue,
+  // stalling the wave before its MFMAs (issue is in order). Loads are inline assembly, which the
+  // scheduler does not move, so the step is a chain of regions separated by loads, each with its
+  // own sched_group_barrier pattern. The body is generated by compile-time recursion so that every
+  // accumulator index is a constant.
   constexpr int NM = NI * MJ;   // MFMAs per step
-  using SS = step_sched<NM, NF, LPS, Elem<T>::kMfmaPerStep>;
-  auto read_frag = [&](const uint8_t* stage, auto Qc) -> uint4 {
-    constexpr int q = decltype(Qc)::value;
-    if constexpr (q < MJ) return *reinterpret_cast<const uint4*>(stage + swz(wm * 128 + q * 16 + fr, fg));
-    else return *reinterpret_cast<const uint4*>(stage + A_BYTES + swz(brow_of(q - MJ) + fr, fg));
-  };
-  auto body = [&](auto self, auto Mc, const uint8_t* next, const Dma& dma, uint4 (&cur)[NF],
-                  uint4 (&nxt)[NF]) -> void {
+  auto body = [&](auto self, auto Lc, auto Sc, auto Mc, const uint8_t* ua, const uint8_t* ub, const Dma& ds,
+                  const Dma& dl, uint4 (&cur)[NF], uint4 (&nxt)[NF]) -> void {
+    constexpr int NL = decltype(Lc)::value;   // loads in this step: an S unit then an L unit, or none
+    using SS = step_sched<NM, NF, NL, Elem<T>::kMfmaPerStep>;
     constexpr int m = decltype(Mc)::value;
     if constexpr (m < NM) {
       constexpr int d = SS::load_at(m);
       if constexpr (d >= 0) {
         SS::template region<SS::load_pos(d - 1), m>();
-        dma_one(dma, std::integral_constant<int, d>{});
+        if constexpr (d < S_LD) {
+          if constexpr (B_LONG) dma_a(ds, std::integral_constant<int, d>{});
+          else dma_b(ds, std::integral_constant<int, d>{});
+        } else {
+          if constexpr (B_LONG) dma_b(dl, std::integral_constant<int, d - S_LD>{});
+          else dma_a(dl, std::integral_constant<int, d - S_LD>{});
+        }
       }
       constexpr int q = SS::read_at_q(m);   // the read that belongs right before MFMA m, if any
-      if constexpr (q >= 0) nxt[q] = read_frag(next, std::integral_constant<int, q>{});
+      if constexpr (q >= 0) nxt[q] = read_frag(ua, ub, Sc, std::integral_constant<int, q>{});
       constexpr int i = m / MJ, j = m % MJ;
       acc[i][j] = mfma16(cur[MJ + i], cur[j], acc[i][j], T());
-      self(self, std::integral_constant<int, m + 1>{}, next, dma, cur, nxt);
+      self(self, Lc, Sc, std::integral_constant<int, m + 1>{}, ua, ub, ds, dl, cur, nxt);
     } else {
-      SS::template region<SS::load_pos(LPS - 1), NM>();
+      SS::template region<SS::load_pos(NL - 1), NM>();
     }
   };
-  // step t: wait for stage t + 1 (stages t + 2 .. t + 4 may stay in flight), synchronise, then the
-  // body.
-  auto step = [&](const uint8_t* next, uint32_t refill, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
+  // Ring: unit u (L_p = 2p, S_p = 2p + 1) sits in slot u % 5. During block p the slots hold L_p and
+  // S_p (being read), L_{p+1} and S_{p+1}, and L_{p+2}.
+  // First step of block p: its second step's fragments come from L_p and S_p, which every wave has
+  // seen since the previous barrier: no load, no wait for memory, no barrier.
+  auto step0 = [&](const uint8_t* ul, const uint8_t* us, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): cur is in registers
-    wait_vmem<3 * LPS>();
+    const Dma none{};
+    body(body, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+         B_LONG ? us : ul, B_LONG ? ul : us, none, none, cur, nxt);
+  };
+  // Second step of block p: wait for L_{p+1} and S_{p+1} (L_{p+2}, issued after them, may stay in
+  // flight), synchronise (L_p and S_p are then free: every wave has read its fragments of block p),
+  // load S_{p+2} into the slot of L_p and L_{p+3} into the slot of S_p, and read the first step's
+  // fragments of block p + 1.
+  auto step1 = [&](const uint8_t* nul, const uint8_t* nus, uint32_t slot_lp, uint32_t slot_sp, uint4 (&cur)[NF],
+                   uint4 (&nxt)[NF]) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_vmem<L_LD>();
     ring_barrier();
-    const Dma dma = next_dma(refill);
-    body(body, std::integral_constant<int, 0>{}, next, dma, cur, nxt);
+    const Dma ds = B_LONG ? next_a(slot_lp) : next_b(slot_lp);
+    const Dma dl = B_LONG ? next_b(slot_sp) : next_a(slot_sp);
+    body(body, std::integral_constant<int, A_LD + B_LD>{}, std::integral_constant<int, 0>{},
+         std::integral_constant<int, 0>{}, B_LONG ? nus : nul, B_LONG ? nul : nus, ds, dl, cur, nxt);
   };
 
   uint4 fa[NF], fb[NF];
   const uint32_t l0 = lds_addr(smem0), l1 = lds_addr(smem1), l2 = lds_addr(smem2), l3 = lds_addr(smem3),
                  l4 = lds_addr(smem4);
-  issue_all(next_dma(l0));
-  issue_all(next_dma(l1));
-  issue_all(next_dma(l2));
-  issue_all(next_dma(l3));
-  issue_all(next_dma(l4));
-  wait_vmem<4 * LPS>();
+  auto issue_l = [&](uint32_t slot) {
+    if constexpr (B_LONG) issue_b(next_b(slot));
+    else issue_a(next_a(slot));
+  };
+  auto issue_s = [&](uint32_t slot) {
+    if constexpr (B_LONG) issue_a(next_a(slot));
+    else issue_b(next_b(slot));
+  };
+  issue_l(l0);   // L_0
+  issue_s(l1);   // S_0
+  issue_l(l2);   // L_1
+  issue_s(l3);   // S_1
+  issue_l(l4);   // L_2
+  wait_vmem<2 * L_LD + S_LD>();   // L_0 and S_0
   ring_barrier();
-  read_frags(smem0, fa);
-  // stage t sits in slot t % 5; the fragment buffers alternate, so ten steps bring both back
-  for (int kt = 0; kt < nk; kt += 2 * kStages) {
-    step(smem1, l0, fa, fb);
-    if (kt + 1 < nk) step(smem2, l1, fb, fa);
-    if (kt + 2 < nk) step(smem3, l2, fa, fb);
-    if (kt + 3 < nk) step(smem4, l3, fb, fa);
-    if (kt + 4 < nk) step(smem0, l4, fa, fb);
-    if (kt + 5 < nk) step(smem1, l0, fb, fa);
-    if (kt + 6 < nk) step(smem2, l1, fa, fb);
-    if (kt + 7 < nk) step(smem3, l2, fb, fa);
-    if (kt + 8 < nk) step(smem4, l3, fa, fb);
-    if (kt + 9 < nk) step(smem0, l4, fb, fa);
+  if constexpr (B_LONG) read_all(read_all, std::integral_constant<int, 0>{}, smem1, smem0, fa);
+  else read_all(read_all, std::integral_constant<int, 0>{}, smem0, smem1, fa);
+  // block p reads L_p, S_p from slots (2p) % 5, (2p + 1) % 5: five blocks bring the pattern back
+  for (int pb = 0; pb < nu; pb += kUnits) {
+    step0(smem0, smem1, fa, fb);
+    step1(smem2, smem3, l0, l1, fb, fa);
+    if (pb + 1 < nu) {
+      step0(smem2, smem3, fa, fb);
+      step1(smem4, smem0, l2, l3, fb, fa);
+    }
+    if (pb + 2 < nu) {
+      step0(smem4, smem0, fa, fb);
+      step1(smem1, smem2, l4, l0, fb, fa);
+    }
+    if (pb + 3 < nu) {
+      step0(smem1, smem2, fa, fb);
+      step1(smem3, smem4, l1, l2, fb, fa);
+    }
+    if (pb + 4 < nu) {
+      step0(smem3, smem4, fa, fb);
+      step1(smem0, smem1, l3, l4, fb, fa);
+    }
   }
   wait_vmem<0>();   // no load into LDS may still be in flight when the workgroup ends
 
@@ -466,8 +531,8 @@ static int pick_bn(int kind, int act, const GemmProblem* probs, const int64_t* r
 bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K) {
   (void)kind;
   (void)act;
-  const int bk = kRowB / (dtype == 0 ? 2 : 4);
-  return N > 0 && N % 64 == 0 && K > 0 && K % bk == 0;
+  const int bu = kRowB / (dtype == 0 ? 2 : 4);   // K elements per unit
+  return N > 0 && N % 64 == 0 && K > 0 && K % bu == 0;
 }
 
 template <typename T, int KIND, int ACT, int BN>
@@ -499,6 +564,10 @@ static void launch_kind(const GemmLaunch& la, int kind, int act, int bn, int gri
 hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* probs, const int64_t* rows_ub,
                                const int64_t* mt_hint, int nprob, hipStream_t st) {
   if (nprob < 1 || nprob > 2) return hipErrorInvalidValue;
+  const int bu = kRowB / (dtype == 0 ? 2 : 4);   // K elements per unit: a unit never straddles a K segment
+  for (int i = 0; i < nprob; ++i)
+    if (probs[i].K <= 0 || probs[i].K % bu != 0 || probs[i].k_seg <= 0 || probs[i].k_seg % bu != 0)
+      return hipErrorInvalidValue;
   const int bn = pick_bn(kind, act, probs, rows_ub, mt_hint, nprob);
   if (bn == 0) return hipErrorInvalidValue;
   // the problem with the longer K goes first (see the tile decode in the kernel)
