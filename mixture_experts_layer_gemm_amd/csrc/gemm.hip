@@ -14,9 +14,10 @@
 //     so every 16-byte-per-lane load instruction reads 8 full lines (reading 64-byte halves made
 //     twice the L2 requests for the same bytes, and the L2 request rate was the limit).
 //   * The A block (256 token rows) and the B block (BN weight rows) of a K block each fill one
-//     32 KB unit of a five-unit LDS ring, by direct global->LDS loads (no staging registers). One
-//     operand (L) is loaded two blocks ahead, the other (S) one block ahead; the up projections
-//     give the weights the long lead, the down projections the tokens. One barrier per block.
+//     32 KB unit of a five-unit LDS ring, by direct global->LDS loads (no staging registers). The
+//     loads of one operand (L) start three MFMA steps before its first read, those of the other
+//     (S) two; the up projections give the weights the long lead, the down projections the
+//     tokens. Each step carries one unit's loads; one barrier per block.
 //   * The loads of a block and the LDS fragment reads of the next step are spread between the
 //     MFMAs of the current one (sched_group_barrier regions), so issue never stalls on a full queue.
 //   * LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), so the 16-byte
@@ -281,9 +282,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     dma_a(d, std::integral_constant<int, 7>{});
     static_assert(A_LD == 8, "eight loads per A unit");
   };
-  // The ring alternates the units of two operands: L, which is loaded two blocks ahead of its use,
-  // and S, loaded one block ahead (below). The up projections give the weights the longer lead,
-  // the down projections the tokens (measured on the dense SwiGLU up and long-K down shapes).
+  // The ring alternates the units of two operands: L, whose loads start three MFMA steps before
+  // it is first read, and S, two steps (below). The up projections give the weights the longer
+  // lead, the down projections the tokens (measured on the dense SwiGLU up and long-K down shapes).
   constexpr bool B_LONG = KIND == GEMM_UP;
   constexpr int L_LD = B_LONG ? B_LD : A_LD, S_LD = B_LONG ? A_LD : B_LD;
   auto issue_b = [&](const Dma& d) {
@@ -339,19 +340,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int NM = NI * MJ;   // MFMAs per step
   auto body = [&](auto self, auto Lc, auto Sc, auto Mc, const uint8_t* ua, const uint8_t* ub, const Dma& ds,
                   const Dma& dl, uint4 (&cur)[NF], uint4 (&nxt)[NF]) -> void {
-    constexpr int NL = decltype(Lc)::value;   // loads in this step: an S unit then an L unit, or none
+    constexpr int KL = decltype(Lc)::value;   // -1: the loads of an L unit; -2: of an S unit
+    constexpr int NL = KL == -1 ? L_LD : S_LD;
     using SS = step_sched<NM, NF, NL, Elem<T>::kMfmaPerStep>;
     constexpr int m = decltype(Mc)::value;
     if constexpr (m < NM) {
       constexpr int d = SS::load_at(m);
       if constexpr (d >= 0) {
         SS::template region<SS::load_pos(d - 1), m>();
-        if constexpr (d < S_LD) {
+        if constexpr (KL == -2) {
           if constexpr (B_LONG) dma_a(ds, std::integral_constant<int, d>{});
           else dma_b(ds, std::integral_constant<int, d>{});
         } else {
-          if constexpr (B_LONG) dma_b(dl, std::integral_constant<int, d - S_LD>{});
-          else dma_a(dl, std::integral_constant<int, d - S_LD>{});
+          if constexpr (B_LONG) dma_b(dl, std::integral_constant<int, d>{});
+          else dma_a(dl, std::integral_constant<int, d>{});
         }
       }
       constexpr int q = SS::read_at_q(m);   // the read that belongs right before MFMA m, if any
@@ -364,28 +366,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     }
   };
   // Ring: unit u (L_p = 2p, S_p = 2p + 1) sits in slot u % 5. During block p the slots hold L_p and
-  // S_p (being read), L_{p+1} and S_{p+1}, and L_{p+2}.
+  // S_p (being read), L_{p+1}, S_{p+1} and L_{p+2}.
   // First step of block p: its second step's fragments come from L_p and S_p, which every wave has
-  // seen since the previous barrier: no load, no wait for memory, no barrier.
-  auto step0 = [&](const uint8_t* ul, const uint8_t* us, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
+  // seen since the previous barrier, so there is no wait for memory and no barrier; it loads
+  // L_{p+2} into the slot of S_{p-1}, free since that barrier.
+  auto step0 = [&](const uint8_t* ul, const uint8_t* us, uint32_t slot_sprev, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): cur is in registers
-    const Dma none{};
-    body(body, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
-         B_LONG ? us : ul, B_LONG ? ul : us, none, none, cur, nxt);
+    const Dma dl = B_LONG ? next_b(slot_sprev) : next_a(slot_sprev);
+    body(body, std::integral_constant<int, -1>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{},
+         B_LONG ? us : ul, B_LONG ? ul : us, dl, dl, cur, nxt);
   };
   // Second step of block p: wait for L_{p+1} and S_{p+1} (L_{p+2}, issued after them, may stay in
   // flight), synchronise (L_p and S_p are then free: every wave has read its fragments of block p),
-  // load S_{p+2} into the slot of L_p and L_{p+3} into the slot of S_p, and read the first step's
-  // fragments of block p + 1.
-  auto step1 = [&](const uint8_t* nul, const uint8_t* nus, uint32_t slot_lp, uint32_t slot_sp, uint4 (&cur)[NF],
-                   uint4 (&nxt)[NF]) {
+  // load S_{p+2} into the slot of L_p, and read the first step's fragments of block p + 1.
+  auto step1 = [&](const uint8_t* nul, const uint8_t* nus, uint32_t slot_lp, uint4 (&cur)[NF], uint4 (&nxt)[NF]) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     wait_vmem<L_LD>();
     ring_barrier();
     const Dma ds = B_LONG ? next_a(slot_lp) : next_b(slot_lp);
-    const Dma dl = B_LONG ? next_b(slot_sp) : next_a(slot_sp);
-    body(body, std::integral_constant<int, A_LD + B_LD>{}, std::integral_constant<int, 0>{},
-         std::integral_constant<int, 0>{}, B_LONG ? nus : nul, B_LONG ? nul : nus, ds, dl, cur, nxt);
+    body(body, std::integral_constant<int, -2>{}, std::integral_constant<int, 0>{},
+         std::integral_constant<int, 0>{}, B_LONG ? nus : nul, B_LONG ? nul : nus, ds, ds, cur, nxt);
   };
 
   uint4 fa[NF], fb[NF];
@@ -402,31 +402,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   issue_l(l0);   // L_0
   issue_s(l1);   // S_0
   issue_l(l2);   // L_1
-  issue_s(l3);   // S_1
-  issue_l(l4);   // L_2
-  wait_vmem<2 * L_LD + S_LD>();   // L_0 and S_0
+  issue_s(l3);   // S_1 (L_2 comes with the first step)
+  wait_vmem<L_LD + S_LD>();   // L_0 and S_0
   ring_barrier();
   if constexpr (B_LONG) read_all(read_all, std::integral_constant<int, 0>{}, smem1, smem0, fa);
   else read_all(read_all, std::integral_constant<int, 0>{}, smem0, smem1, fa);
-  // block p reads L_p, S_p from slots (2p) % 5, (2p + 1) % 5: five blocks bring the pattern back
+  // block p reads L_p, S_p from slots (2p) % 5, (2p + 1) % 5, and S_{p-1} sat in slot (2p - 1) % 5:
+  // five blocks bring the pattern back
   for (int pb = 0; pb < nu; pb += kUnits) {
-    step0(smem0, smem1, fa, fb);
-    step1(smem2, smem3, l0, l1, fb, fa);
+    step0(smem0, smem1, l4, fa, fb);
+    step1(smem2, smem3, l0, fb, fa);
     if (pb + 1 < nu) {
-      step0(smem2, smem3, fa, fb);
-      step1(smem4, smem0, l2, l3, fb, fa);
+      step0(smem2, smem3, l1, fa, fb);
+      step1(smem4, smem0, l2, fb, fa);
     }
     if (pb + 2 < nu) {
-      step0(smem4, smem0, fa, fb);
-      step1(smem1, smem2, l4, l0, fb, fa);
+      step0(smem4, smem0, l3, fa, fb);
+      step1(smem1, smem2, l4, fb, fa);
     }
     if (pb + 3 < nu) {
-      step0(smem1, smem2, fa, fb);
-      step1(smem3, smem4, l1, l2, fb, fa);
+      step0(smem1, smem2, l0, fa, fb);
+      step1(smem3, smem4, l1, fb, fa);
     }
     if (pb + 4 < nu) {
-      step0(smem3, smem4, fa, fb);
-      step1(smem0, smem1, l3, l4, fb, fa);
+      step0(smem3, smem4, l2, fa, fb);
+      step1(smem0, smem1, l3, fb, fa);
     }
   }
   wait_vmem<0>();   // no load into LDS may still be in flight when the workgroup ends
