@@ -56,6 +56,11 @@ def parse():
                     help="DICE denoising-step loop: reuse fraction and time per step under three policies")
     ap.add_argument("--des-fit", action="store_true",
                     help="fit the DES per-expert latency model f(c) = a*c + b on the streaming kernels")
+    ap.add_argument("--dense", action="store_true",
+                    help="the grouped GEMM kernels on dense single-expert problems, with torch.matmul on the same "
+                         "shapes for context")
+    ap.add_argument("--zero-operands", action="store_true",
+                    help="with --dense: zero tokens and weights (the clock then stays at its peak)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (3 times): the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
@@ -151,6 +156,82 @@ def des_fit(args):
                       "bytes_per_expert": bytes_per_expert,
                       "b_as_bandwidth_GBps": round(bytes_per_expert / (float(coef[1]) * 1e-6) / 1e9, 1)}),
           flush=True)
+
+
+def dense_gemm(args):
+    """The grouped GEMM kernels on dense problems: one heavy expert that every token takes (top-1 of
+    1), so through moe_layer_forward the up projection is a plain S x (m*f) x d GEMM over the tokens
+    in order (m = 2 for SwiGLU) and the down projection S x d x f. Their rates come from the
+    library's own event timing of the two launches. torch.matmul (the vendor GEMM: bf16 out, no
+    activation, no gather) runs the same shapes on operands drawn the same way, for context. One
+    JSON line per shape."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_gemm_amd as moe
+    from synth import WORKLOADS, gen_layer_inputs, gen_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S = 16384
+
+    def up(bits):
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+        return t.zero_() if args.zero_operands else t
+
+    def vendor_us(a, b):
+        for _ in range(3):
+            torch.matmul(a, b.t())
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.matmul(a, b.t())
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    for d, f, act in ((1152, 4608, "swiglu"), (1536, 6144, "gelu"), (4608, 4608, "swiglu")):
+        spec = WORKLOADS["dit_moe_xl"].replace(S=S, d=d, f=f, act=act, E_heavy=1, n_shared=0, k=1)
+        inp = gen_layer_inputs(spec, seed=0)
+        b = inp.bits
+        t = {"w_router": up(b["w_router.0"]), "w1": up(b["w1.0"]), "w2": up(b["w2.0"])}
+        if act == "swiglu":
+            t["w3"] = up(b["w3.0"])
+        x = up(b["x"])
+        desc = moe.desc_from_spec(spec)
+        ws = moe.workspace(desc, device=dev)
+        rb = moe.alloc_routing(desc, device=dev)
+        y = torch.empty_like(x)
+        wts = moe.weights_struct(t)
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            moe.moe_layer_forward(desc, x, wts, None, None, rb.struct, None, None, y, ws, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        moe.moe_profile_begin()
+        for _ in range(args.steps):
+            moe.moe_layer_forward(desc, x, wts, None, None, rb.struct, None, None, y, ws, stream=stream.cuda_stream)
+        prof = moe.moe_profile_end()
+        torch.cuda.synchronize()
+        m = 2 if act == "swiglu" else 1
+        up_us = prof["gemm_up"][0] * 1e3 / prof["gemm_up"][1]
+        down_us = prof["gemm_down"][0] * 1e3 / prof["gemm_down"][1]
+        flops_up, flops_down = 2.0 * S * d * f * m, 2.0 * S * d * f
+        # vendor GEMMs on the same shapes: tokens x (gate and up rows side by side), hidden x W2
+        w_up = t["w1"].reshape(-1, d)
+        if act == "swiglu":
+            w_up = torch.cat([w_up, t["w3"].reshape(-1, d)], 0)
+        h = up(gen_tensor(np.random.default_rng(1), (S, f), 1.0, "bf16")[1])
+        v_up, v_down = vendor_us(x, w_up.contiguous()), vendor_us(h, t["w2"].reshape(-1, f).contiguous())
+        print(json.dumps({"problem": f"{act} d={d} f={f} S={S}", "operands": "zero" if args.zero_operands else "random",
+                          "up": f"{S} x {m * f} x {d}", "up_us": round(up_us, 1),
+                          "up_tflops": round(flops_up / up_us / 1e6, 1),
+                          "down": f"{S} x {d} x {f}", "down_us": round(down_us, 1),
+                          "down_tflops": round(flops_down / down_us / 1e6, 1),
+                          "vendor_up_tflops": round(flops_up / v_up / 1e6, 1),
+                          "vendor_down_tflops": round(flops_down / v_down / 1e6, 1)}), flush=True)
+        del t, x, y, ws, rb, h, w_up
+        torch.cuda.empty_cache()
 
 
 def dice_steps(args):
@@ -268,6 +349,9 @@ def main():
         return
     if args.dice_steps:
         dice_steps(args)
+        return
+    if args.dense:
+        dense_gemm(args)
         return
 
     import numpy as np
