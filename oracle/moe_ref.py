@@ -421,6 +421,33 @@ def stack_forward(spec, W, x, act_bf16=True):
 
 
 # --------------------------------------------------------------------------------------------
+# Attention-residual aggregation over block states (the block-level step next to the MoE layer)
+# --------------------------------------------------------------------------------------------
+
+
+def attnres_aggregate(states, query, eps=1e-6):
+    """Depth aggregation of block states by a learned pseudo-query.
+
+    [MMOE] 方法论, attention-residual aggregation: before a sub-layer, a learned pseudo-query
+    aggregates the list of completed block states; the forward keeps those states and the current
+    partial state as recurrent state. The page gives no formula. Reading [R33]: for every token s,
+    each state v_j (the completed block states, then the current partial state) gets the score
+    z_j = q . v_j / sqrt(mean(v_j^2) + eps) (the query against the state's RMS-normalised copy);
+    the weights are the softmax of z over j, and the result is sum_j alpha_j v_j over the raw
+    states.
+
+    states: [n, S, d]; query: [d]. Returns (out [S, d], alpha [S, n]).
+    """
+    V = np.asarray(states, F64)
+    q = np.asarray(query, F64)
+    rms = np.sqrt(np.mean(V * V, axis=2) + eps)          # [n, S]
+    z = (V @ q) / rms                                    # [n, S]
+    alpha = softmax(z.T)                                 # [S, n], softmax over the states
+    out = np.einsum("sj,jsd->sd", alpha, V)
+    return out, alpha
+
+
+# --------------------------------------------------------------------------------------------
 # DES latency model (measurement model, not a kernel)
 # --------------------------------------------------------------------------------------------
 

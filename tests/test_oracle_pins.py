@@ -412,3 +412,76 @@ def test_bf16_round_reference_values():
     assert orc.bf16_round(1.0 + 2 ** -8 + 2 ** -12) == 1.0 + 2 ** -7
     assert orc.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6     # tie -> even mantissa
     assert orc.bf16_round(-3.0) == -3.0
+
+
+# ------------------------------------------------------------------------------ attention-residual aggregation
+
+
+def _states(rng, n, S, d, scale=1.0):
+    return rng.standard_normal((n, S, d)) * scale
+
+
+def test_attnres_single_state_is_identity():
+    rng = np.random.default_rng(0)
+    V = _states(rng, 1, 5, 16)
+    out, alpha = orc.attnres_aggregate(V, rng.standard_normal(16))
+    assert np.array_equal(alpha, np.ones((5, 1)))
+    assert np.array_equal(out, V[0])
+
+
+def test_attnres_zero_query_is_mean_and_identical_states_pass_through():
+    rng = np.random.default_rng(1)
+    V = _states(rng, 4, 6, 8)
+    out, alpha = orc.attnres_aggregate(V, np.zeros(8))
+    assert np.allclose(alpha, 0.25, atol=1e-15, rtol=0)
+    assert np.allclose(out, V.mean(axis=0), atol=1e-14, rtol=0)
+    same = np.repeat(V[:1], 3, axis=0)
+    out2, _ = orc.attnres_aggregate(same, rng.standard_normal(8) * 5)
+    assert np.allclose(out2, V[0], atol=1e-14, rtol=0)
+
+
+def test_attnres_two_orthogonal_states_give_the_logistic():
+    """v0 = a e_0, v1 = b e_1 in d = 4, q = t e_0, eps = 0: v0's RMS is |a| / 2, so z_0 = 2 t
+    sign(a) and z_1 = 0, and the two-state softmax gives alpha_0 = sigma(2 t sign(a)), tabulated."""
+    table = {z: p for z, p in _gold("logistic.json")["values"]}
+    d = 4
+    for a, b, t, zz in ((3.0, -7.0, 0.5, 1.0), (0.25, 2.0, 1.0, 2.0), (-5.0, 1.0, 0.5, -1.0), (2.0, 9.0, 0.0, 0.0)):
+        V = np.zeros((2, 1, d))
+        V[0, 0, 0] = a
+        V[1, 0, 1] = b
+        q = np.zeros(d)
+        q[0] = t
+        out, alpha = orc.attnres_aggregate(V, q, eps=0.0)
+        p0 = table[zz]
+        assert abs(alpha[0, 0] - p0) <= 1e-12 and abs(alpha[0, 1] - (1 - p0)) <= 1e-12
+        assert abs(out[0, 0] - p0 * a) <= 1e-12 * abs(a)
+        assert abs(out[0, 1] - (1 - p0) * b) <= 1e-12 * abs(b)
+        assert out[0, 2] == 0 and out[0, 3] == 0
+
+
+def test_attnres_scores_ignore_state_scale_and_order():
+    """The keys are RMS-normalised, so scaling a state by c > 0 leaves every weight unchanged
+    (eps = 0) while the output takes the scaled state; permuting the states permutes the weights
+    and leaves the output unchanged."""
+    rng = np.random.default_rng(2)
+    V = _states(rng, 5, 7, 12)
+    q = rng.standard_normal(12)
+    out, alpha = orc.attnres_aggregate(V, q, eps=0.0)
+    W = V.copy()
+    W[2] *= 37.0
+    out2, alpha2 = orc.attnres_aggregate(W, q, eps=0.0)
+    assert np.allclose(alpha2, alpha, atol=1e-14, rtol=0)
+    assert np.allclose(out2 - out, alpha[:, 2:3] * 36.0 * V[2], atol=1e-12, rtol=0)
+    perm = [3, 0, 4, 2, 1]
+    out3, alpha3 = orc.attnres_aggregate(V[perm], q, eps=0.0)
+    assert np.allclose(alpha3, alpha[:, perm], atol=1e-15, rtol=0)
+    assert np.allclose(out3, out, atol=1e-13, rtol=0)
+
+
+def test_attnres_is_a_convex_combination():
+    rng = np.random.default_rng(3)
+    V = _states(rng, 6, 9, 10, scale=3.0)
+    out, alpha = orc.attnres_aggregate(V, rng.standard_normal(10) * 2)
+    assert np.all(alpha > 0)
+    assert np.allclose(alpha.sum(axis=1), 1.0, atol=1e-15, rtol=0)
+    assert np.all(out <= V.max(axis=0) + 1e-12) and np.all(out >= V.min(axis=0) - 1e-12)
