@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--dense", action="store_true",
                     help="the grouped GEMM kernels on dense single-expert problems, with torch.matmul on the same "
                          "shapes for context")
+    ap.add_argument("--attnres", action="store_true",
+                    help="attention-residual aggregation over n block states (MMOE width, 16384 tokens): "
+                         "HBM throughput per n")
     ap.add_argument("--zero-operands", action="store_true",
                     help="with --dense: zero tokens and weights (the clock then stays at its peak)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -234,6 +237,49 @@ def dense_gemm(args):
         torch.cuda.empty_cache()
 
 
+def attnres_bench(args):
+    """Attention-residual aggregation ("MMOE: Modernizing Diffusion Transformers with Efficient Expert
+    Design", 方法论) on the MMOE shape: 64 x 256 = 16384 tokens, d = 1152, bf16, with n = 5, 9 and 17
+    states (4, 8, 16 completed block states and the partial one). The kernel reads every state once
+    and writes the output: (n + 1) * S * d * 2 bytes per call, its HBM roofline. Successive calls
+    take their states from a pool of 17 distinct ones (641 MB), so the 256 MB MALL cannot hold a
+    call's inputs. Times are the library's event timing of the launches. One JSON line per n."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_layer_gemm_amd as moe
+    from synth import gen_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S, d = 16384, 1152
+    rng = np.random.default_rng(0)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    pool = [up(gen_tensor(rng, (S, d), 1.0, "bf16")[1]) for _ in range(17)]
+    q = up(gen_tensor(rng, (d,), 1.0 / np.sqrt(d), "bf16")[1])
+    out = torch.empty((S, d), dtype=torch.bfloat16, device=dev)
+    for n in (5, 9, 17):
+        sets = [[pool[(i * n + j) % len(pool)] for j in range(n)] for i in range(max(args.steps, args.warmup))]
+        for i in range(args.warmup):
+            moe.moe_attnres_aggregate(moe.MOE_BF16, S, d, sets[i], q, 1e-6, out)
+        torch.cuda.synchronize()
+        moe.moe_profile_begin()
+        for i in range(args.steps):
+            moe.moe_attnres_aggregate(moe.MOE_BF16, S, d, sets[i], q, 1e-6, out)
+        prof = moe.moe_profile_end()
+        torch.cuda.synchronize()
+        us = prof["attnres"][0] * 1e3 / prof["attnres"][1]
+        nbytes = (n + 1) * S * d * 2 + d * 2
+        gbs = nbytes / us / 1e3
+        print(json.dumps({"kernel": "attnres", "states": n, "tokens": S, "d": d, "dtype": "bf16", "us": round(us, 2),
+                          "bytes_per_call": nbytes,
+                          "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}}), flush=True)
+
+
 def dice_steps(args):
     """The DICE step loop on one GPU ("DICE: Staleness-Centric Optimizations for Parallel Diffusion MoE
     Inference", 关键设计). A stack of 4 DiT-MoE-XL-shaped MoE layers (residual stream) runs T = 10
@@ -352,6 +398,9 @@ def main():
         return
     if args.dense:
         dense_gemm(args)
+        return
+    if args.attnres:
+        attnres_bench(args)
         return
 
     import numpy as np

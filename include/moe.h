@@ -167,6 +167,19 @@ moe_status moe_layer_forward(const moe_desc *desc, const void *x, const moe_weig
                              const float *prev_logits, float *logits_out, moe_routing *routing, void *cache,
                              const void *residual, void *y, void *ws, size_t ws_bytes, void *stream);
 
+/* Attention-residual aggregation ("MMOE: Modernizing Diffusion Transformers with Efficient Expert
+ * Design", 方法论: before a sub-layer a learned pseudo-query aggregates the completed block states,
+ * which the forward keeps with the current partial state). The page gives no formula; per token s
+ * this computes, over the n states v_j (states[j], each [S,d] of dtype, row-major; the completed
+ * states, then the partial one):
+ *   z_j = query . v_j[s] / sqrt(mean(v_j[s]^2) + eps),  out[s] = sum_j softmax_j(z)_j * v_j[s].
+ * states: [host] array of n device pointers (1 <= n <= 64); query [d] and out [S,d] are device
+ * buffers of dtype (MOE_BF16 or MOE_F32); every buffer is 16-byte aligned; out may not alias a
+ * state. fp32 arithmetic, one rounding to dtype. S = 0 does nothing. MOE_EINVAL for null or
+ * misaligned pointers, n < 1, d <= 0, S < 0 or a negative or non-finite eps; MOE_EUNSUPPORTED for n > 64, d not a multiple of 8 (bf16) / 4 (fp32), or d > 4096. */
+moe_status moe_attnres_aggregate(int32_t dtype, int32_t S, int32_t d, int32_t n, const void *const *states,
+                                 const void *query, float eps, void *out, void *stream);
+
 /* Static description of a status code. Thread-safe. */
 const char *moe_strerror(int status);
 

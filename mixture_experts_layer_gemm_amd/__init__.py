@@ -18,7 +18,7 @@ __all__ = [
     "MoeDesc", "MoeRouting", "MoeWeights", "MoeError", "MoeLibraryMissing",
     "lib", "lib_path", "EXPORTS",
     "moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-    "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end",
+    "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_attnres_aggregate",
 ]
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
@@ -29,7 +29,8 @@ MOE_F_INPUT_PROBS, MOE_F_SYNC_DEBUG, MOE_F_FORCE_TILED, MOE_F_FORCE_STREAM = 0x1
 MOE_F_ROUTE_MULTI = 0x20
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_profile_entry")
+           "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_profile_entry",
+           "moe_attnres_aggregate")
 
 _i32, _f32, _u32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p
 
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [P(MoeDesc), _vp, P(MoeWeights), _vp, _vp, P(MoeRouting), _vp, _vp, _vp,
                                         _vp, ctypes.c_size_t, _vp]
+        L.moe_attnres_aggregate.restype = ctypes.c_int
+        L.moe_attnres_aggregate.argtypes = [_i32, _i32, _i32, _i32, P(_vp), _vp, _f32, _vp, _vp]
         L.moe_strerror.restype = ctypes.c_char_p
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_profile_begin.restype = ctypes.c_int
@@ -140,6 +143,16 @@ def moe_route(desc, logits, routing: MoeRouting, ws, ws_bytes=None, stream=None,
     nb = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
     st = lib().moe_route(ctypes.byref(desc), _ptr(logits), ctypes.byref(routing), _ptr(ws), nb, _stream(stream))
     return _check(st, "moe_route", raise_on_error)
+
+
+def moe_attnres_aggregate(dtype: int, S: int, d: int, states, query, eps: float, out, stream=None,
+                          raise_on_error=True) -> int:
+    """Attention-residual aggregation: ``states`` is a sequence of n device tensors (or addresses)
+    of [S, d]; their addresses go to the library as a host array."""
+    ptrs = (_vp * max(1, len(states)))(*[_ptr(t) for t in states])
+    st = lib().moe_attnres_aggregate(int(dtype), int(S), int(d), len(states), ptrs if len(states) else None,
+                                     _ptr(query), float(eps), _ptr(out), _stream(stream))
+    return _check(st, "moe_attnres_aggregate", raise_on_error)
 
 
 def moe_dispatch(desc, x, routing: MoeRouting, x_perm, stream=None, raise_on_error=True) -> int:

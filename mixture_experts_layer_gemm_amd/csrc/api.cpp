@@ -602,6 +602,28 @@ moe_status moe_profile_entry(int i, const char** name, double* total_ms, int32_t
   return MOE_OK;
 }
 
+moe_status moe_attnres_aggregate(int32_t dtype, int32_t S, int32_t d, int32_t n, const void* const* states,
+                                 const void* query, float eps, void* out, void* stream) {
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_EINVAL;
+  if (S < 0 || d <= 0 || n < 1 || !states || !query || !out || !(eps >= 0.f) || !std::isfinite(eps))
+    return MOE_EINVAL;
+  if (n > kAttnMaxStates || !attnres_supported(dtype, d)) return MOE_EUNSUPPORTED;
+  auto misaligned = [](const void* p) { return ((uintptr_t)p & 15u) != 0; };
+  if (misaligned(query) || misaligned(out)) return MOE_EINVAL;
+  AttnResArgs a{};
+  for (int j = 0; j < n; ++j) {
+    if (!states[j] || misaligned(states[j])) return MOE_EINVAL;
+    a.states[j] = states[j];
+  }
+  a.query = query;
+  a.out = out;
+  a.n = n;
+  a.S = S;
+  a.d = d;
+  a.eps = eps;
+  return launch_attnres(dtype, a, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
 const char* moe_strerror(int status) {
   switch (status) {
     case MOE_OK: return "ok";

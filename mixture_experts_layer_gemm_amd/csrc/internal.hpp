@@ -148,4 +148,18 @@ bool stream_gemm_supported(int dtype, int kind, int act, int N, int K);
 
 hipError_t launch_fill_u32(uint32_t* p, uint32_t v, size_t n, hipStream_t st);
 
+// ---------------------------------------------------------------------------------------------
+// Attention-residual aggregation: out[s] = sum_j softmax_j(q . v_j[s] / rms(v_j[s]))_j v_j[s] over
+// n states of [S, d] (dtype), per token.
+constexpr int kAttnMaxStates = 64;
+struct AttnResArgs {
+  const void* states[kAttnMaxStates];
+  const void* query;   // [d]
+  void* out;           // [S, d]
+  int32_t n, S, d;
+  float eps;
+};
+bool attnres_supported(int dtype, int d);
+hipError_t launch_attnres(int dtype, const AttnResArgs& a, hipStream_t st);
+
 }  // namespace moe

@@ -141,3 +141,25 @@ def test_binding_raises_with_status():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_route(_desc(k=0), FAKE, moe.MoeRouting(), FAKE, 1, stream=0)
     assert ei.value.status == moe.MOE_EINVAL
+
+
+def test_attnres_argument_checks():
+    """Invalid arguments are rejected on the host, before anything is launched (no GPU needed)."""
+    a, q, o = 0x10000, 0x20000, 0x30000   # never dereferenced: every call below fails validation
+    call = moe.moe_attnres_aggregate
+    assert call(moe.MOE_BF16, 4, 64, [], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a, None], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a], None, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a], q, 1e-6, None, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, -1, 64, [a], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 0, [a], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a], q, -1.0, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a], q, float("nan"), o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(7, 4, 64, [a], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a + 8], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 64, [a], q + 2, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert call(moe.MOE_BF16, 4, 60, [a], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EUNSUPPORTED
+    assert call(moe.MOE_BF16, 4, 8192, [a], q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EUNSUPPORTED
+    assert call(moe.MOE_BF16, 4, 64, [a] * 65, q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EUNSUPPORTED
+    with pytest.raises(moe.MoeError):
+        call(moe.MOE_BF16, 4, 64, [], q, 1e-6, o, stream=0)
