@@ -26,7 +26,7 @@
 //     columns of one row: 8-byte (bf16) / 16-byte (fp32) stores.
 //   * Gather fused into the A loads: row r reads x[row_token[r]].
 //   * Tile order: workgroup b runs on XCD b % 8; tiles are renumbered so each XCD owns a
-//     contiguous range, swept as 8 m-tiles x all n-tiles, which keeps an expert's weight panels and
+//     contiguous range, swept as 4 m-tiles x all n-tiles, which keeps an expert's weight panels and
 //     token panels in one XCD's L2.
 //   * The expert of an m-tile comes from a scalar scan of ceil(count_e / 256) over experts.
 #include <algorithm>
@@ -46,7 +46,7 @@ constexpr int kUnitB = 32768;
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
 constexpr int kWaves = 4;           // 2 x 2 wave grid, one wave per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kGM = 8;              // m-tiles per sweep group
+constexpr int kGM = 4;              // m-tiles per sweep group
 
 struct GemmLaunch {
   GemmProblem p0, p1;
