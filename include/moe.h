@@ -53,7 +53,9 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,        /* null pointer, inconsistent sizes, k/vote_k/m_core out of range, C rounds to 0 */
-  MOE_EUNSUPPORTED = -2,  /* dtype / activation / shape alignment this library does not implement */
+  MOE_EUNSUPPORTED = -2,  /* dtype / activation / shape alignment this library does not implement;
+                             e.g. the tiled expert GEMMs (used when experts get many rows) need
+                             d and d_ff to be multiples of 64 */
   MOE_EWORKSPACE = -3,    /* ws_bytes < moe_workspace_bytes(desc) or ws not 256-byte aligned */
   MOE_EHIP = -4           /* a HIP launch or runtime error (the call's work may be partly enqueued) */
 } moe_status;

@@ -72,6 +72,7 @@ UNSUPPORTED = [
     dict(k=17, E_heavy=40),                         # ... but k > 16 is not implemented
     dict(mode=moe.MOE_EXPERT_CHOICE, n_zero=1),     # zero-computation experts under expert choice
     dict(d_ff=4600),                                # GEMM tiles need d_ff % 64
+    dict(d=1120),                                   # the GEMM's K blocks (up: K = d) need d % 64 in bf16
 ]
 
 
