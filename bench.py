@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--attnres", action="store_true",
                     help="attention-residual aggregation over n block states (MMOE width, 16384 tokens): "
                          "HBM throughput per n")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured once into a HIP graph and replayed (adds a 'graph' field)")
     ap.add_argument("--zero-operands", action="store_true",
                     help="with --dense: zero tokens and weights (the clock then stays at its peak)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -462,7 +464,7 @@ def main():
     logits = [torch.empty((spec.S, spec.E_routed), dtype=torch.float32, device=dev) for _ in range(spec.n_layers)]
     setup_s = time.time() - t0
 
-    def step(i):
+    def step(i, st=None):
         h = x
         prev = None
         for layer in range(spec.n_layers):
@@ -470,7 +472,7 @@ def main():
             res = h if spec.n_layers > 1 else None
             moe.moe_layer_forward(desc, h, w, prev, logits[layer] if spec.n_layers > 1 else None,
                                   rb.struct if layer == spec.n_layers - 1 else None, cache, res, hs[layer], ws,
-                                  stream=stream.cuda_stream)
+                                  stream=(st or stream).cuda_stream)
             h = hs[layer]
             prev = logits[layer]
 
@@ -487,6 +489,31 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3 / args.steps
     ms = ev0.elapsed_time(ev1) / args.steps
+
+    # the same steps captured once into a HIP graph (one step per weight copy) and replayed: the
+    # launch gaps between the layer's kernels go away
+    graph = None
+    if args.graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(copies):
+                step(i, side)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // copies)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        gev0, gev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        gev0.record()
+        for _ in range(reps):
+            g.replay()
+        gev1.record()
+        torch.cuda.synchronize()
+        gms = gev0.elapsed_time(gev1) / (reps * copies)
+        graph = {"ms_per_step": round(gms, 4), "value": round(spec.S / (gms / 1e3), 1), "steps": reps * copies}
 
     # per-kernel times: a second pass with event pairs attached to every launch
     moe.moe_profile_begin()
@@ -560,6 +587,8 @@ def main():
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
+    if graph is not None:
+        out["graph"] = graph
     print(json.dumps(out), flush=True)
 
 
