@@ -126,6 +126,17 @@ def test_stream_shapes(d, f, act, S, m_core):
     _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
 
 
+@pytest.mark.parametrize("mode", ["tc", "ec"])
+def test_single_expert_layer_is_a_dense_mlp(mode):
+    """One heavy expert that every token takes (top-1 of 1, or expert choice with C clipped to S):
+    the layer is a dense MLP over the tokens in order, the shape of bench.py --dense."""
+    base = WORKLOADS["dit_moe_xl"] if mode == "tc" else WORKLOADS["ec_dit"]
+    spec = base.replace(S=700, E_heavy=1, n_shared=0, k=1)
+    _, rt, _ = _layer_case(spec)
+    if mode == "ec":
+        assert rt["C"] == spec.S
+
+
 def test_light_experts_only_layer():
     """No heavy experts: identity, zero and constant experts plus a shared expert."""
     spec = WORKLOADS["mmoe"].replace(S=500, d=256, f=512, E_heavy=0)
