@@ -101,3 +101,16 @@ def test_attnres_large_scores_stay_finite():
     got = _run(vals, bits, q_big, None, "f32")
     assert np.all(np.isfinite(got))
     _check(got, ref, vals, "f32", rel_amax=5e-3)
+
+
+def test_attnres_bench_shape_sampled():
+    """The shape bench.py --attnres times (16384 tokens, d = 1152, 17 states, bf16), checked on 512
+    sampled tokens: each token's output depends only on that token's rows."""
+    S, d, n = 16384, 1152, 17
+    say(f"attnres full size S={S} d={d} n={n}")
+    vals, bits, qv, qb = _make(123, n, S, d, "bf16")
+    got = _run(vals, bits, qv, qb, "bf16")
+    rows = np.sort(np.random.default_rng(7).choice(S, 512, replace=False))
+    sub = [v[rows] for v in vals]
+    ref, _ = orc.attnres_aggregate(np.stack(sub), qv)
+    _check(got[rows], ref, sub, "bf16")
