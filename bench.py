@@ -9,7 +9,12 @@ Prints one JSON line: tokens/s, the roofline of the dominant kernel (its duratio
 HIP events attached to its launches on its own stream), and the fp64 CPU oracle timed on a bounded
 sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--graph]
+
+Other modes (each prints its own JSON lines): --des-fit (the DES per-expert latency model fitted on
+the streaming kernels), --dice-steps (DICE reuse over a denoising-step loop), --dense (the GEMM
+kernels on dense single-expert problems, with torch.matmul on the same shapes), --attnres (the
+attention-residual aggregation's HBM rate), --calibrate-copy (a plain copy for the HBM counters).
 """
 from __future__ import annotations
 
