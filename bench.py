@@ -143,8 +143,9 @@ def des_fit(args):
                 call(i)
             prof = moe.moe_profile_end()
             torch.cuda.synchronize()
-            t_us = sum(prof[k][0] * 1e3 / prof[k][1] for k in ("stream_up", "stream_down") if k in prof)
-            layer_us = sum(v[0] * 1e3 / v[1] for v in prof.values())
+            # per layer call (a kernel may be launched more than once per call)
+            t_us = sum(prof[k][0] * 1e3 / args.steps for k in ("stream_up", "stream_down") if k in prof)
+            layer_us = sum(v[0] * 1e3 / args.steps for v in prof.values())
             counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
             r, e = int(counts.sum()), int(np.count_nonzero(counts))
             rows.append(r)
@@ -224,8 +225,9 @@ def dense_gemm(args):
         prof = moe.moe_profile_end()
         torch.cuda.synchronize()
         m = 2 if act == "swiglu" else 1
-        up_us = prof["gemm_up"][0] * 1e3 / prof["gemm_up"][1]
-        down_us = prof["gemm_down"][0] * 1e3 / prof["gemm_down"][1]
+        # per layer call: a projection may run as two launches (a column remainder split off)
+        up_us = prof["gemm_up"][0] * 1e3 / args.steps
+        down_us = prof["gemm_down"][0] * 1e3 / args.steps
         flops_up, flops_down = 2.0 * S * d * f * m, 2.0 * S * d * f
         # vendor GEMMs on the same shapes: tokens x (gate and up rows side by side), hidden x W2
         w_up = t["w1"].reshape(-1, d)
@@ -526,7 +528,10 @@ def main():
         step(i)
     prof = moe.moe_profile_end()
     torch.cuda.synchronize()
-    kernels = {k: {"avg_us": round(v[0] * 1e3 / v[1], 2), "launches": v[1]} for k, v in prof.items()}
+    # avg_us: per layer call (the sum of a kernel's launches in one call: a GEMM projection may be split
+    # into two launches); launches: over the whole pass
+    calls = args.steps * spec.n_layers
+    kernels = {k: {"avg_us": round(v[0] * 1e3 / calls, 2), "launches": v[1]} for k, v in prof.items()}
 
     # algorithmic work per launch from the actual routing
     n_rows = int(rb["n_rows"][0].item())
@@ -549,7 +554,7 @@ def main():
     dom = max(cand, key=lambda k: prof[k][0]) if cand else None
     roofline = None
     if dom:
-        avg_s = prof[dom][0] / prof[dom][1] / 1e3
+        avg_s = prof[dom][0] / calls / 1e3   # per layer call, like work_per_launch
         bound, amount = work[dom]
         if bound == "mfma":
             peak = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
