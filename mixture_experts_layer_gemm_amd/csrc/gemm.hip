@@ -433,6 +433,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 
   // ---- epilogue: lane holds rows (m) = wm*128 + j*16 + fr, columns 4*fg + t of n-subtile i
   const int64_t col_base = (int64_t)g * P.c_gcol;
+  if constexpr (SWIGLU && BN == 256 && sizeof(T) == 2) {
+    // SwiGLU with 256-wide tiles: each wave's 128 x 64 bf16 outputs (128 bytes per row) go through
+    // LDS, so that every store instruction writes 8 whole 128-byte lines instead of 16 rows x 32
+    // bytes. 16-byte chunk c of staged row r sits at slot c ^ (r & 7). The ring is free once every
+    // wave has passed this barrier (their last fragment reads are done).
+    ring_barrier();
+    uint8_t* stage = (wave < 2 ? smem0 : smem1) + (wave & 1) * (128 * 128);
+#pragma unroll
+    for (int j = 0; j < MJ; ++j)
+#pragma unroll
+      for (int i = 0; i < NI / 2; ++i) {
+        float h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) h[t] = silu(acc[i + NI / 2][j][t]) * acc[i][j][t];
+        uint2 v;
+        v.x = pack2_bf16(h[0], h[1]);
+        v.y = pack2_bf16(h[2], h[3]);
+        const int r = j * 16 + fr, c = 2 * i + (fg >> 1);
+        *reinterpret_cast<uint2*>(stage + r * 128 + ((c ^ (r & 7)) << 4) + (fg & 1) * 8) = v;
+      }
+    const int c = lane & 7;
+    const int n = nt * (BN / 2) + wn * (BN / 4) + c * 8;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = q * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 128 + ((c ^ (r & 7)) << 4));
+      const int ml = wm * 128 + r;
+      if (ml >= rows || n >= P.N) continue;
+      *reinterpret_cast<uint4*>((T*)P.C + (row0 + ml) * P.ldc + col_base + n) = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < MJ; ++j) {
     const int ml = wm * 128 + j * 16 + fr;
