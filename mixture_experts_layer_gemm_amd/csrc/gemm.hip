@@ -23,7 +23,9 @@
 //   * LDS rows are 128 B; 16-byte chunk c of row r sits at slot c ^ ((r >> 1) & 7), so the 16-byte
 //     fragment reads of 16 consecutive rows cover all banks once.
 //   * Weights are MFMA operand P and tokens operand Q, so each lane ends with 4 consecutive output
-//     columns of one row: 8-byte (bf16) / 16-byte (fp32) stores.
+//     columns of one row: 8-byte (bf16) / 16-byte (fp32) stores. With 256-wide tiles the SwiGLU up
+//     and the fp32 down outputs are staged through the freed LDS ring first, so that each store
+//     instruction writes whole 128-byte lines.
 //   * Gather fused into the A loads: row r reads x[row_token[r]].
 //   * Tile order: workgroup b runs on XCD b % 8; tiles are renumbered so each XCD owns a
 //     contiguous range, swept as 4 m-tiles x all n-tiles, which keeps an expert's weight panels and
@@ -453,6 +455,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
         const int r = j * 16 + fr, c = 2 * i + (fg >> 1);
         *reinterpret_cast<uint2*>(stage + r * 128 + ((c ^ (r & 7)) << 4) + (fg & 1) * 8) = v;
       }
+    asm volatile("" ::: "memory");   // the wave's LDS accesses run in order; keep the compiler's too
     const int c = lane & 7;
     const int n = nt * (BN / 2) + wn * (BN / 4) + c * 8;
 #pragma unroll
@@ -462,6 +465,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
       const int ml = wm * 128 + r;
       if (ml >= rows || n >= P.N) continue;
       *reinterpret_cast<uint4*>((T*)P.C + (row0 + ml) * P.ldc + col_base + n) = v;
+    }
+    return;
+  }
+  if constexpr (KIND == GEMM_DOWN && BN == 256) {
+    // fp32 outputs with 256-wide tiles: each wave's 128 x 128 outputs go through its own 32 KB unit
+    // in two halves of 64 rows (512 bytes per row), 16-byte chunk c of row r at slot c ^ (r & 15);
+    // each store instruction then writes 2 rows x 512 bytes (8 whole lines) instead of 16 rows x
+    // 64 bytes.
+    ring_barrier();
+    uint8_t* stage = wave == 0 ? smem0 : wave == 1 ? smem1 : wave == 2 ? smem2 : smem3;
+    const int c = lane & 31;
+    const int n = nt * BN + wn * (BN / 2) + c * 4;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int jj = 0; jj < MJ / 2; ++jj)
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int j = hf * (MJ / 2) + jj;
+          const int r = jj * 16 + fr, ch = 4 * i + fg;
+          *reinterpret_cast<float4*>(stage + r * 512 + ((ch ^ (r & 15)) << 4)) =
+              make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int q = 0; q < 32; ++q) {
+        const int r = q * 2 + (lane >> 5);
+        const float4 v = *reinterpret_cast<const float4*>(stage + r * 512 + ((c ^ (r & 15)) << 4));
+        const int ml = wm * 128 + hf * 64 + r;
+        if (ml >= rows || n >= P.N) continue;
+        *reinterpret_cast<float4*>((float*)P.C + (row0 + ml) * P.ldc + col_base + n) = v;
+      }
+      asm volatile("" ::: "memory");   // the second half overwrites what the first half read
     }
     return;
   }
