@@ -394,7 +394,7 @@ def read_traffic(kernel, workload):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
