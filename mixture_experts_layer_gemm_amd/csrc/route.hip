@@ -26,76 +26,86 @@ extern "C" __device__ __attribute__((const)) float __ockl_wfred_add_f32(float);
 namespace moe {
 
 // =============================================================================================
-// Router GEMM. A workgroup computes 16 tokens x (16 * ET) experts (grid.y covers the rest). Its W
-// waves split the K axis (wave w takes K steps w, w + W, ...), so each wave has only a few
+// Router GEMM. A workgroup computes 16 * TT tokens x (16 * ET) experts (grid.y covers the rest).
+// Its W waves split the K axis (wave w takes K steps w, w + W, ...), so each wave has only a few
 // dependent load rounds; the partial sums are then added in LDS in wave order (a fixed order:
 // results do not depend on timing). 16x16 MFMA tiles with operand P = W_r rows (16 experts) and
 // operand Q = x rows (16 tokens): each lane ends with 4 consecutive experts of one token. x is read
-// once from HBM per expert slice; W_r stays in cache.
-template <typename T, int ET>
+// once from HBM per expert slice; W_r stays in cache, and each of its fragments serves the TT
+// token tiles (with many experts its cache reads would otherwise outnumber those of x).
+template <typename T, int ET, int TT>
 __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const T* __restrict__ w,
                                                  const float* __restrict__ prev, float* __restrict__ logits,
                                                  int S, int d, int E) {
   constexpr int EPC = Elem<T>::kPer16B;
   constexpr int STEP = 4 * EPC;   // K elements per MFMA step
   constexpr int EW = ET * 16;     // experts per workgroup
-  extern __shared__ float s_part[];   // [W][16][EW]
+  constexpr int TW = TT * 16;     // tokens per workgroup
+  extern __shared__ float s_part[];   // [W][TW][EW]
   const int W = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, g = lane >> 4;
-  const int s0 = blockIdx.x * 16;
+  const int s0 = blockIdx.x * TW;
   const int e0 = blockIdx.y * EW;
-  const T* xrow = x + (size_t)min(s0 + r, S - 1) * d + g * EPC;
+  const T* xrow[TT];
+#pragma unroll
+  for (int p = 0; p < TT; ++p) xrow[p] = x + (size_t)min(s0 + p * 16 + r, S - 1) * d + g * EPC;
   const T* wrow[ET];
   bool wok[ET];
-  floatx4_t acc[ET];
+  floatx4_t acc[TT][ET];
 #pragma unroll
   for (int q = 0; q < ET; ++q) {
     const int e = e0 + q * 16 + r;
     wok[q] = e < E;
     wrow[q] = w + (size_t)min(e, E - 1) * d + g * EPC;
-    acc[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int p = 0; p < TT; ++p) acc[p][q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
   const int nsteps = d / STEP;
 #pragma unroll 2
   for (int t = wave; t < nsteps; t += W) {
     const size_t kk = (size_t)t * STEP;
-    const uint4 xv = *reinterpret_cast<const uint4*>(xrow + kk);
+    uint4 xv[TT];
+#pragma unroll
+    for (int p = 0; p < TT; ++p) xv[p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
 #pragma unroll
     for (int q = 0; q < ET; ++q) {
       uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
       if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
-      acc[q] = mfma16(wv, xv, acc[q], T());
+#pragma unroll
+      for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(wv, xv[p], acc[p][q], T());
     }
   }
-  float* mine = s_part + (size_t)wave * 16 * EW;
+  float* mine = s_part + (size_t)wave * TW * EW;
 #pragma unroll
-  for (int q = 0; q < ET; ++q)
+  for (int p = 0; p < TT; ++p)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) mine[r * EW + q * 16 + 4 * g + t] = acc[q][t];
+    for (int q = 0; q < ET; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) mine[(p * 16 + r) * EW + q * 16 + 4 * g + t] = acc[p][q][t];
   __syncthreads();
   const int ne = min(EW, E - e0);
-  for (int o = threadIdx.x; o < 16 * ne; o += blockDim.x) {
+  for (int o = threadIdx.x; o < TW * ne; o += blockDim.x) {
     const int tr = o / ne, el = o - tr * ne;
     const int st = s0 + tr, e = e0 + el;
     if (st >= S) continue;
     float v = 0.f;
-    for (int q = 0; q < W; ++q) v += s_part[((size_t)q * 16 + tr) * EW + el];
+    for (int q = 0; q < W; ++q) v += s_part[((size_t)q * TW + tr) * EW + el];
     if (prev) v += prev[(size_t)st * E + e];
     logits[(size_t)st * E + e] = v;
   }
 }
 
-template <typename T, int ET>
+template <typename T, int ET, int TT>
 static void router_t(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
                      hipStream_t st) {
   constexpr int STEP = 4 * Elem<T>::kPer16B;
   const int nsteps = d / STEP;
   // about 4 K steps per wave; the partial sums of all waves fit in 64 KB of LDS
-  const int W = std::max(1, std::min({16, nsteps / 4, 64 / ET}));
-  const size_t lds = (size_t)W * 16 * ET * 16 * sizeof(float);
-  const dim3 grid((S + 15) / 16, (E + ET * 16 - 1) / (ET * 16));
-  auto kfn = k_router<T, ET>;
+  const int W = std::max(1, std::min({16, nsteps / 4, 64 / (ET * TT)}));
+  const size_t lds = (size_t)W * 16 * TT * ET * 16 * sizeof(float);
+  const dim3 grid((S + 16 * TT - 1) / (16 * TT), (E + ET * 16 - 1) / (ET * 16));
+  auto kfn = k_router<T, ET, TT>;
   MOE_LAUNCH("router", kfn, grid, 64 * W, lds, st, (const T*)x, (const T*)w_router, prev, logits, S, d, E);
 }
 
@@ -103,12 +113,13 @@ template <typename T>
 static void router_dt(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
                       hipStream_t st) {
   // few tokens: one 16-expert tile per workgroup, for more workgroups; many tokens: all experts in
-  // one workgroup, so x is read once
-  if (E <= 16 || S <= 1024) router_t<T, 1>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 32) router_t<T, 2>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 64) router_t<T, 4>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 128) router_t<T, 8>(x, w_router, prev, logits, S, d, E, st);
-  else router_t<T, 16>(x, w_router, prev, logits, S, d, E, st);
+  // one workgroup, so x is read once, and 32 tokens per workgroup, so each W_r fragment read from
+  // the cache serves two token tiles
+  if (E <= 16 || S <= 1024) router_t<T, 1, 1>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 32) router_t<T, 2, 2>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 64) router_t<T, 4, 2>(x, w_router, prev, logits, S, d, E, st);
+  else if (E <= 128) router_t<T, 8, 2>(x, w_router, prev, logits, S, d, E, st);
+  else router_t<T, 16, 1>(x, w_router, prev, logits, S, d, E, st);   // two tiles would spill
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits, int S,

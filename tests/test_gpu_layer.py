@@ -126,6 +126,15 @@ def test_stream_shapes(d, f, act, S, m_core):
     _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
 
 
+@pytest.mark.parametrize("E", [20, 48, 100, 200])
+def test_router_expert_slices_many_tokens(E):
+    """Above 1024 tokens a router workgroup covers 32 tokens and all experts (16-expert tiles x 2,
+    4 or 8), or 16 tokens and 256 experts: logits and the layer against the oracle for each slice
+    width, with a ragged last token tile (1500 = 46 x 32 + 28)."""
+    spec = WORKLOADS["dit_moe_xl"].replace(S=1500, d=256, f=256, E_heavy=E, n_shared=0)
+    _layer_case(spec)
+
+
 @pytest.mark.parametrize("mode", ["tc", "ec"])
 def test_single_expert_layer_is_a_dense_mlp(mode):
     """One heavy expert that every token takes (top-1 of 1, or expert choice with C clipped to S):
