@@ -205,7 +205,15 @@ __global__ __launch_bounds__(kCsrTok) void k_ec_csr(ECArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s0 = blockIdx.x * kCsrTok;
   int before = 0;
-  for (int i = threadIdx.x; i < s0; i += kCsrTok) before += a.tok_cnt[i];
+  int i = threadIdx.x;
+  for (; i + 7 * kCsrTok < s0; i += 8 * kCsrTok) {   // eight loads in flight (s0 is a multiple of kCsrTok)
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = a.tok_cnt[i + j * kCsrTok];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) before += v[j];
+  }
+  for (; i < s0; i += kCsrTok) before += a.tok_cnt[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
   const int s = s0 + threadIdx.x;
