@@ -428,10 +428,15 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scan(PermuteArgs a, int n
   __shared__ int tot[kPermMaxE];
   for (int e = threadIdx.x; e < a.E_heavy; e += kPermThreads) {
     int run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int c = a.blk_cnt[(size_t)b * a.E_heavy + e];
-      a.blk_cnt[(size_t)b * a.E_heavy + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {   // eight loads in flight, then the eight bases in order
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = b0 + j < nblk ? a.blk_cnt[(size_t)(b0 + j) * a.E_heavy + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < nblk) a.blk_cnt[(size_t)(b0 + j) * a.E_heavy + e] = run;
+        run += c[j];
+      }
     }
     tot[e] = run;
   }
