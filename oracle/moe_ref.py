@@ -169,6 +169,13 @@ def des_seq_core(filter_keys, k_seq):
     return np.unique(T).astype(np.int64)
 
 
+def des_seq_counts(filter_keys, k_seq, E):
+    """For each expert, the number of tokens whose local top-k_seq holds it ([DES] 2.3: the local
+    selections whose union is the core). The core is the set of experts with a nonzero count."""
+    T = rank_desc(filter_keys)[:, :k_seq]
+    return np.bincount(T.ravel(), minlength=E).astype(np.int64)
+
+
 def core_reroute(keys, P, core, k, renorm):
     """Each token re-activates its top-k' experts inside the core set, k' = min(k, |core|)
     [DES] 4.3 [R12]. Keys restricted to the core decide (ties to lower index); weights are the
@@ -329,13 +336,19 @@ def route(spec, L=None, P=None, input_probs=False, vote_dtype=F64):
         votes, core = des_vote(keys, P, spec.vote_k, spec.m_core, vote_dtype=vote_dtype)
         idx, w = core_reroute(keys, P, core, spec.k, spec.renorm)
         out.update(idx=idx, w=w, votes=votes, core=core)
+    elif spec.mode == "des_seq":
+        # [DES] 2.3 core = union of each token's top-k_seq (k_seq = spec.vote_k, the local selection
+        # count of 3.1); then, as in 4.3, every token re-activates its top-k inside that core
+        core = des_seq_core(keys, spec.vote_k)
+        idx, w = core_reroute(keys, P, core, spec.k, spec.renorm)
+        out.update(idx=idx, w=w, votes=des_seq_counts(keys, spec.vote_k, E), core=core)
     elif spec.mode == "ec":
         C = ec_capacity(S, E, spec.capacity_factor)
         tokens, gates = ec_select(P, C)
         out.update(C=C, tokens=tokens, gates=gates)
     else:
         raise ValueError(spec.mode)
-    if spec.mode in ("tc", "des"):
+    if spec.mode in ("tc", "des", "des_seq"):
         out["reuse"] = (out["pmax"] < spec.reuse_tau) if spec.reuse_tau > 0 else np.zeros(S, bool)
     return out
 
@@ -402,10 +415,11 @@ def bf16_round(a):
     return u.astype(np.uint32).view(np.float32).astype(F64)
 
 
-def stack_forward(spec, W, x, act_bf16=True):
+def stack_forward(spec, W, x, act_bf16=True, gate_residual=True):
     """``spec.n_layers`` MoE layers on a residual stream h_{l+1} = h_l + y_l, each router adding
-    the previous layer's logits ([MMOE] gate-residual routing) [R17, R18]. The stream is stored in
-    the layer precision (bf16 for a bf16 workload) between layers. Returns per-layer results."""
+    the previous layer's logits ([MMOE] gate-residual routing) [R17, R18] unless ``gate_residual``
+    is False (a DiT-MoE stack). The stream is stored in the layer precision (bf16 for a bf16
+    workload) between layers. Returns per-layer results."""
     h = np.asarray(x, F64)
     prev = None
     outs = []
@@ -415,9 +429,50 @@ def stack_forward(spec, W, x, act_bf16=True):
         r["h_in"] = h
         r["h_out"] = h_next
         outs.append(r)
-        prev = r["logits"]
+        prev = r["logits"] if gate_residual else None
         h = h_next
     return outs
+
+
+def dice_step_loop(spec, W, xs, tau, stride, reuse_layers, act_bf16=True, rt_hook=None):
+    """DICE denoising-step loop on one device ([DICE] 关键设计).
+
+    ``xs`` are the latent tokens of the successive steps t = 0, 1, ...; each step runs the
+    ``spec.n_layers`` MoE layers on a residual stream (no gate residual: a DiT-MoE stack). Every
+    layer keeps a cache of its routed output (交织并行: only the combine result is kept) across
+    steps. At step t, layer l lets tokens whose top routing score is below ``tau`` reuse that
+    cache (条件通信: low-score tokens take the stale result, high-score ones are recomputed)
+    when l is in ``reuse_layers`` and t is not a multiple of ``stride``; otherwise every token is
+    recomputed (the stride refresh, and 选择性同步: layers outside ``reuse_layers`` stay
+    synchronous). Fresh tokens write their routed part into the cache, rounded to the storage
+    precision (bf16 for a bf16 workload); reused tokens leave it alone. The stream between layers
+    is stored in the same precision.
+
+    ``rt_hook(t, layer, L, rt, spec_l)`` may replace the routing decisions of a layer call (a test
+    that accepts the other side's choice on near-ties). Returns, per step, a list of per-layer
+    dicts: h_in, y, routed, cache (after the call), reuse (the mask used).
+    """
+    rnd = bf16_round if act_bf16 else (lambda a: np.asarray(a, F64))
+    caches = [None] * spec.n_layers
+    steps = []
+    for t, x in enumerate(xs):
+        h = np.asarray(x, F64)
+        per = []
+        for layer in range(spec.n_layers):
+            fresh = (layer not in reuse_layers) or (t % stride == 0)
+            sp = spec.replace(reuse_tau=0.0 if fresh else float(tau))
+            L = router_logits(h, W.w_router[layer])
+            rt = route(sp, L=L)
+            if rt_hook is not None:
+                rt = rt_hook(t, layer, L, rt, sp)
+            r = layer_forward(sp, W, h, layer=layer, cache=caches[layer], residual=h, rt=rt)
+            caches[layer] = np.where(rt["reuse"][:, None], caches[layer], rnd(r["routed"])) \
+                if caches[layer] is not None else rnd(r["routed"])
+            y = rnd(r["y"])
+            per.append({"h_in": h, "y": y, "routed": r["routed"], "cache": caches[layer], "reuse": rt["reuse"]})
+            h = y
+        steps.append(per)
+    return steps
 
 
 # --------------------------------------------------------------------------------------------

@@ -36,11 +36,11 @@ class LayerSpec:
     n_const: int = 0            # ... and learned-constant
     n_shared: int = 0           # always-on experts, weight 1
     act: str = "gelu"           # "gelu" (erf) | "gelu_tanh" | "swiglu"
-    mode: str = "tc"            # "tc" token choice | "ec" expert choice | "des" DES-Vote
+    mode: str = "tc"            # "tc" token choice | "ec" expert choice | "des" DES-Vote | "des_seq" DES-Seq
     k: int = 2                  # token-choice / DES re-route top-k
     renorm: bool = True         # renormalise the selected weights
     capacity_factor: float = 2.0
-    vote_k: int = 0             # DES filter K
+    vote_k: int = 0             # DES-Vote filter K; DES-Seq local selection count k_seq
     m_core: int = 0             # DES core-set size
     reuse_tau: float = 0.0      # DICE-style low-score reuse threshold (0 = off)
     dtype: str = "bf16"         # "bf16" | "f32"
@@ -74,9 +74,14 @@ WORKLOADS: dict[str, LayerSpec] = {
                                mode="des", k=8, renorm=True, vote_k=8, m_core=16),
     "des_vote_b050": LayerSpec("des_vote_b050", S=32, d=2048, f=1024, E_heavy=64, act="swiglu",
                                mode="des", k=8, renorm=True, vote_k=8, m_core=32),
-    # DES-Seq on the same block: every token keeps its own top-8; the experts loaded are the union.
-    "des_seq": LayerSpec("des_seq", S=32, d=2048, f=1024, E_heavy=64, act="swiglu", mode="tc", k=8,
-                         renorm=True),
+    # DES-Seq on the same block: the core is the union of every token's top-2 (local selection
+    # count k_seq = 2); tokens then re-route top-8 inside it.
+    "des_seq": LayerSpec("des_seq", S=32, d=2048, f=1024, E_heavy=64, act="swiglu", mode="des_seq", k=8,
+                         renorm=True, vote_k=2),
+    # The vanilla block the DES variants are measured against: every token its own top-8; the
+    # experts loaded are their union.
+    "vanilla_top8": LayerSpec("vanilla_top8", S=32, d=2048, f=1024, E_heavy=64, act="swiglu", mode="tc", k=8,
+                              renorm=True),
     # MMOE MoE++: 64 x 256 tokens, d=1152, 16 heavy GELU experts + identity/zero/constant + 1 shared,
     # top-2 over 19 with gate residual, 4 stacked layers.
     "mmoe": LayerSpec("mmoe", S=16384, d=1152, f=4608, E_heavy=16, n_identity=1, n_zero=1, n_const=1,

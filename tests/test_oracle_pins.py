@@ -172,6 +172,37 @@ def test_single_expert_is_dense_mlp(mode, act):
     assert np.allclose(r["y"], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_router_logits_hand_worked():
+    """L = x . W_r^T with W_r stored [E, d]: x = (1, 2), expert rows (1, 0), (0, 1), (1, 1), (-2, 0.5)
+    give L = (1, 2, 3, -1); the gate residual adds the previous logits elementwise."""
+    x = np.array([[1.0, 2.0]])
+    w = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0], [-2.0, 0.5]])
+    assert orc.router_logits(x, w).tolist() == [[1.0, 2.0, 3.0, -1.0]]
+    assert orc.router_logits(x, w, np.array([[0.5, -2.0, 0.0, 1.0]])).tolist() == [[1.5, 0.0, 3.0, 0.0]]
+
+
+def test_expert_choice_two_experts_hand_affinities():
+    """Two experts, f_c = 1.5, S = 4: C = 3. Logits ln 3 / ln 1, ln 1 / ln 3, 0 / 0, ln 7 / ln 1 give
+    affinities (3/4, 1/4), (1/4, 3/4), (1/2, 1/2), (7/8, 1/8). Expert 0 takes tokens 3, 0, 2 and
+    expert 1 tokens 1, 2, 0, so token 0 gets 3/4 F_0 + 1/4 F_1, token 1 gets 3/4 F_1, token 2 gets
+    1/2 F_0 + 1/2 F_1 and token 3 gets 7/8 F_0 (EC-DiT 核心公式: the output sums A_{s,i} FFN_i over
+    the experts that chose s)."""
+    spec = LayerSpec(name="ec2", S=4, d=8, f=12, E_heavy=2, act="gelu", mode="ec", capacity_factor=1.5,
+                     dtype="f32")
+    W = gen_layer_inputs(spec, seed=14, std=0.4)
+    x = W.x.astype(np.float64)
+    L = np.log(np.array([[3.0, 1.0], [1.0, 3.0], [1.0, 1.0], [7.0, 1.0]]))
+    rt = orc.route(spec, L=L)
+    assert rt["C"] == 3
+    assert rt["tokens"].tolist() == [[0, 2, 3], [0, 1, 2]]
+    y = orc.layer_forward(spec, W, x, rt=rt)["y"]
+    F = [_textbook_ffn(x, W.w1[0][i].astype(np.float64), None, W.w2[0][i].astype(np.float64), "gelu")
+         for i in range(2)]
+    want = np.stack([0.75 * F[0][0] + 0.25 * F[1][0], 0.75 * F[1][1], 0.5 * F[0][2] + 0.5 * F[1][2],
+                     0.875 * F[0][3]])
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-13)
+
+
 # ------------------------------------------------------------------------------ DES
 
 
@@ -251,6 +282,64 @@ def test_des_seq_is_union_of_topk():
     assert list(core) == want
 
 
+def _padded_route_bruteforce(L, core, k):
+    """Per token, the top-min(k, |core|) experts inside the core by brute force (key sum, then the
+    lexicographically smallest tuple), in key order."""
+    out = []
+    for s in range(L.shape[0]):
+        kk = min(k, len(core))
+        sub = _brute_topk(L[s, core], kk)
+        chosen = [int(core[i]) for i in sub]
+        chosen.sort(key=lambda e: (-L[s, e], e))
+        out.append(chosen)
+    return np.array(out, dtype=np.int64)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_des_seq_route_matches_bruteforce(seed):
+    """DES-Seq (Dynamic Expert Sharing, 2.3; 3.1 local count k_seq; 4.3 re-activate top-k in the core):
+    the core is the union of each token's top-k_seq, every routed slot lies in it, and each token's
+    slots are its brute-force top-k inside the core. Integer logits give exact ties."""
+    rng = np.random.default_rng(40 + seed)
+    N, E = int(rng.integers(2, 7)), int(rng.integers(5, 11))
+    L = rng.integers(-3, 4, size=(N, E)).astype(float)
+    for k_seq in range(1, E + 1):
+        for k in (2, 4):
+            if k > E:
+                continue
+            spec = LayerSpec(name="dseq", S=N, d=8, f=8, E_heavy=E, act="gelu", mode="des_seq", k=k,
+                             vote_k=k_seq, dtype="f32")
+            rt = orc.route(spec, L=L)
+            want_core = sorted({e for s in range(N) for e in _brute_topk(L[s], k_seq)})
+            assert list(rt["core"]) == want_core
+            assert np.array_equal(np.flatnonzero(rt["votes"]), want_core)
+            assert rt["votes"].sum() == N * k_seq
+            assert np.array_equal(rt["idx"], _padded_route_bruteforce(L, np.array(want_core), k))
+            assert np.allclose(rt["w"].sum(1), 1.0)
+
+
+def test_des_seq_reduces_to_token_choice_when_k_seq_covers_k():
+    """With k_seq >= k every token's own top-k lies in the core, so DES-Seq is vanilla top-k."""
+    rng = np.random.default_rng(9)
+    L = rng.standard_normal((32, 64))
+    base = LayerSpec(name="dseq", S=32, d=8, f=8, E_heavy=64, act="gelu", mode="tc", k=8, dtype="f32")
+    tc = orc.route(base, L=L)
+    for k_seq in (8, 12, 64):
+        rt = orc.route(base.replace(mode="des_seq", vote_k=k_seq), L=L)
+        assert np.array_equal(rt["idx"], tc["idx"]) and np.allclose(rt["w"], tc["w"], atol=1e-15)
+
+
+def test_des_seq_core_smaller_than_k():
+    """One token with k_seq = 2 < k = 4: the core has 2 experts and the token keeps both."""
+    L = np.array([[0.1, 2.0, -1.0, 1.5, 0.0]])
+    spec = LayerSpec(name="dseq", S=1, d=8, f=8, E_heavy=5, act="gelu", mode="des_seq", k=4, vote_k=2, dtype="f32")
+    rt = orc.route(spec, L=L)
+    assert list(rt["core"]) == [1, 3]
+    assert rt["idx"].tolist() == [[1, 3]]
+    e = np.exp(np.array([2.0, 1.5]))
+    assert np.allclose(rt["w"][0], e / e.sum(), atol=1e-15)
+
+
 def test_des_latency_model():
     # f(c) = a c + b for c > 0: two experts with 3 and 5 tokens, one idle.
     assert orc.des_block_latency([3, 0, 5], a=2.0, b=10.0) == (2 * 3 + 10) + (2 * 5 + 10)
@@ -298,6 +387,14 @@ def test_silu_matches_logistic():
 def test_gelu_tanh_close_to_erf_form():
     z = np.linspace(-4, 4, 81)
     assert np.max(np.abs(orc.gelu_tanh(z) - orc.gelu(z))) < 1e-3
+
+
+def test_gelu_tanh_matches_decimal_table():
+    """The tanh form against 40-digit values of the published formula (a wrong constant, such as
+    0.0447 for 0.044715 or 2/pi for sqrt(2/pi), fails by far more than the tolerance)."""
+    g = _gold("gelu_tanh.json")
+    for z, want in g["values"]:
+        assert abs(orc.gelu_tanh(z) - want) <= g["tolerance"] * max(1.0, abs(want)), (z, orc.gelu_tanh(z), want)
 
 
 def test_mlp_hand_worked():
@@ -355,23 +452,86 @@ def test_zero_and_identity_and_const_experts():
 
 
 def test_combine_sensitivity_identity():
-    """d||y|| / d h^e = s^e * y / ||y|| for y = sum_e s^e h^e (DICE, conditional communication)."""
-    rng = np.random.default_rng(11)
-    h = rng.standard_normal((3, 10))           # three expert outputs for one token
-    s = np.array([0.5, 0.3, 0.2])
+    """DICE, conditional communication: for y = sum_e s^e h^e, d||y|| / d h^e = s^e * y / ||y||.
+    Checked through the oracle's layer: three constant experts (their outputs h^e are the vectors
+    v_e, so they can be perturbed directly), top-3 of 3 without renormalisation and hand-chosen
+    logits ln 5, ln 3, ln 2 per token, so the scores are exactly 1/2, 3/10, 1/5."""
+    spec = LayerSpec(name="sens", S=2, d=10, f=8, E_heavy=0, n_const=3, act="gelu", mode="tc", k=3,
+                     renorm=False, dtype="f32")
+    W = gen_layer_inputs(spec, seed=11, std=1.0)
+    L = np.log(np.array([[5.0, 3.0, 2.0], [2.0, 5.0, 3.0]]))
+    rt = orc.route(spec, L=L)
+    s_want = {0: [0.5, 0.3, 0.2], 1: [0.2, 0.5, 0.3]}            # score of expert e for token t
+    for t in range(2):
+        for j in range(3):
+            assert abs(rt["w"][t, j] - s_want[t][rt["idx"][t, j]]) < 1e-15
 
-    def ynorm(hh):
-        return np.linalg.norm((s[:, None] * hh).sum(0))
+    def ynorm(cv, t):
+        W2 = gen_layer_inputs(spec, seed=11, std=1.0)
+        W2.const_vec[0] = cv
+        return np.linalg.norm(orc.layer_forward(spec, W2, W2.x, rt=rt)["y"][t])
 
-    y = (s[:, None] * h).sum(0)
-    eps = 1e-6
-    for e in range(3):
-        for i in range(10):
-            hp, hm = h.copy(), h.copy()
-            hp[e, i] += eps
-            hm[e, i] -= eps
-            fd = (ynorm(hp) - ynorm(hm)) / (2 * eps)
-            assert abs(fd - s[e] * y[i] / np.linalg.norm(y)) < 1e-8
+    cv0 = W.const_vec[0].astype(np.float64)
+    for t in range(2):
+        y = orc.layer_forward(spec, W, W.x, rt=rt)["y"][t]
+        ny = np.linalg.norm(y)
+        assert np.allclose(y, sum(s_want[t][e] * cv0[e] for e in range(3)), atol=1e-15)
+        eps = 1e-6
+        for e in range(3):
+            for i in range(spec.d):
+                cp, cm = cv0.copy(), cv0.copy()
+                cp[e, i] += eps
+                cm[e, i] -= eps
+                fd = (ynorm(cp, t) - ynorm(cm, t)) / (2 * eps)
+                assert abs(fd - s_want[t][e] * y[i] / ny) < 1e-8
+
+
+def test_shared_experts_sum_with_weight_one():
+    """Two always-on shared experts (MMOE 共享专家; the DiT-MoE-XL workload has two): the oracle's
+    shared part is the plain sum of the two dense MLPs, each written out as loops (SwiGLU and GELU),
+    and a layer with only a zero expert routed returns exactly that sum."""
+    for act in ("swiglu", "gelu"):
+        spec = LayerSpec(name="shared2", S=5, d=8, f=12, E_heavy=0, n_zero=1, n_shared=2, act=act, mode="tc",
+                         k=1, dtype="f32")
+        W = gen_layer_inputs(spec, seed=12, std=0.4)
+        x = W.x.astype(np.float64)
+        want = np.zeros((spec.S, spec.d))
+        for i in range(2):
+            w3 = None if W.s_w3[0] is None else W.s_w3[0][i].astype(np.float64)
+            want += _textbook_ffn(x, W.s_w1[0][i].astype(np.float64), w3, W.s_w2[0][i].astype(np.float64), act)
+        assert np.allclose(orc.shared_out(spec, W, 0, x), want, rtol=1e-12, atol=1e-12)
+        # each expert contributes: dropping either one changes the sum
+        one = _textbook_ffn(x, W.s_w1[0][0].astype(np.float64),
+                            None if W.s_w3[0] is None else W.s_w3[0][0].astype(np.float64),
+                            W.s_w2[0][0].astype(np.float64), act)
+        assert np.abs(want - one).max() > 1e-3
+        r = orc.layer_forward(spec, W, x)
+        assert np.all(r["rt"]["idx"] == 0) and np.all(r["routed"] == 0.0)
+        assert np.allclose(r["y"], want, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [False, True])
+def test_top2_two_heavy_experts_hand_logits(renorm):
+    """Top-2 of three heavy experts with hand-chosen logits ln 5, ln 3, ln 2 (permuted per token):
+    probabilities 1/2, 3/10, 1/5, so the two chosen weights are 1/2 and 3/10 (raw) or 5/8 and 3/8
+    (renormalised). The layer must equal that weighted sum of the two chosen experts' dense MLPs,
+    written out as loops."""
+    spec = LayerSpec(name="top2", S=3, d=8, f=12, E_heavy=3, act="gelu", mode="tc", k=2, renorm=renorm,
+                     dtype="f32")
+    W = gen_layer_inputs(spec, seed=13, std=0.4)
+    x = W.x.astype(np.float64)
+    L = np.log(np.array([[5.0, 3.0, 2.0], [2.0, 3.0, 5.0], [3.0, 2.0, 5.0]]))
+    pick = [(0, 1), (2, 1), (2, 0)]
+    wts = (5 / 8, 3 / 8) if renorm else (0.5, 0.3)
+    rt = orc.route(spec, L=L)
+    for t in range(3):
+        assert tuple(rt["idx"][t]) == pick[t]
+        assert np.allclose(rt["w"][t], wts, rtol=0, atol=1e-15)
+    y = orc.layer_forward(spec, W, x, rt=rt)["y"]
+    for t in range(3):
+        want = sum(wj * _textbook_ffn(x[t:t + 1], W.w1[0][e].astype(np.float64), None,
+                                      W.w2[0][e].astype(np.float64), "gelu")[0] for wj, e in zip(wts, pick[t]))
+        assert np.allclose(y[t], want, rtol=1e-12, atol=1e-13)
 
 
 # ------------------------------------------------------------------------------ layer-level
@@ -485,3 +645,81 @@ def test_attnres_is_a_convex_combination():
     assert np.all(alpha > 0)
     assert np.allclose(alpha.sum(axis=1), 1.0, atol=1e-15, rtol=0)
     assert np.all(out <= V.max(axis=0) + 1e-12) and np.all(out >= V.min(axis=0) - 1e-12)
+
+
+# ------------------------------------------------------------------------------ DICE step loop
+
+
+def _dice_spec(**kw):
+    base = dict(name="dice", S=48, d=16, f=24, E_heavy=4, n_shared=1, act="swiglu", mode="tc", k=2, renorm=True,
+                dtype="f32", n_layers=3)
+    base.update(kw)
+    return LayerSpec(**base)
+
+
+def _steps(W, T, drift, seed=21):
+    rng = np.random.default_rng(seed)
+    x = W.x.astype(np.float64)
+    xs = []
+    for _ in range(T):
+        xs.append(x.copy())
+        x = x + drift * rng.standard_normal(x.shape)
+    return xs
+
+
+def test_dice_loop_without_reuse_is_a_fresh_stack_per_step():
+    spec = _dice_spec()
+    W = gen_layer_inputs(spec, seed=22, std=0.3)
+    xs = _steps(W, 4, 0.1)
+    for tau, layers in ((0.3, ()), (0.0, (0, 1, 2))):
+        steps = orc.dice_step_loop(spec, W, xs, tau=tau, stride=3, reuse_layers=layers, act_bf16=False)
+        for t, per in enumerate(steps):
+            fresh = orc.stack_forward(spec, W, xs[t], act_bf16=False, gate_residual=False)
+            for layer in range(spec.n_layers):
+                assert not per[layer]["reuse"].any()
+                assert np.array_equal(per[layer]["y"], fresh[layer]["y"])
+
+
+def test_dice_loop_stationary_input_full_reuse_repeats_step_zero():
+    """tau > 1 reuses every token on non-refresh steps: the routed part is the cache of step 0
+    exactly, so with an unchanged input every step reproduces step 0 bit for bit (fp32 storage)."""
+    spec = _dice_spec()
+    W = gen_layer_inputs(spec, seed=23, std=0.3)
+    xs = [W.x.astype(np.float64)] * 5
+    steps = orc.dice_step_loop(spec, W, xs, tau=1.5, stride=4, reuse_layers=(0, 1, 2), act_bf16=False)
+    for t in range(1, 5):
+        for layer in range(spec.n_layers):
+            if t % 4 != 0:
+                assert steps[t][layer]["reuse"].all()
+                assert np.array_equal(steps[t][layer]["routed"], steps[0][layer]["routed"])
+            assert np.array_equal(steps[t][layer]["y"], steps[0][layer]["y"])
+
+
+def test_dice_loop_reuse_refresh_and_selective_sync():
+    """With a drifting input: on a reuse step, tokens below tau take the previous cache exactly and
+    the others match a fresh computation; refresh steps and the synchronous (deep) layer always
+    match a fresh layer call on their input; caches hold the fresh routed parts."""
+    spec = _dice_spec(E_heavy=8)
+    W = gen_layer_inputs(spec, seed=24, std=0.15)
+    xs = _steps(W, 5, 0.05)
+    tau, stride, layers = 0.3, 3, (0, 1)
+    steps = orc.dice_step_loop(spec, W, xs, tau=tau, stride=stride, reuse_layers=layers, act_bf16=False)
+    n_reused = 0
+    for t, per in enumerate(steps):
+        for layer, r in enumerate(per):
+            h = r["h_in"]
+            fresh = orc.layer_forward(spec, W, h, layer=layer, residual=h)
+            P = fresh["rt"]["P"]
+            reuse = r["reuse"]
+            if layer in layers and t % stride != 0:
+                assert np.array_equal(reuse, P.max(1) < tau)
+                prev = steps[t - 1][layer]["cache"]
+                assert np.array_equal(r["routed"][reuse], prev[reuse])
+                assert np.array_equal(r["cache"][reuse], prev[reuse])
+                n_reused += int(reuse.sum())
+            else:
+                assert not reuse.any()
+            assert np.allclose(r["routed"][~reuse], fresh["routed"][~reuse], rtol=0, atol=1e-14)
+            assert np.array_equal(r["cache"][~reuse], r["routed"][~reuse])
+            assert np.allclose(r["y"], fresh["y"] - fresh["routed"] + r["routed"], rtol=0, atol=1e-13)
+    assert 0 < n_reused < 5 * spec.S * len(layers)
