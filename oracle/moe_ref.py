@@ -253,12 +253,16 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def mlp(xr, w1, w3, w2, act):
+def mlp(xr, w1, w3, w2, act, h_store=None):
     """A heavy expert, the standard MLP of [MMOE] MoE++ (no biases [R20]).
 
     GELU:   W2 . gelu(W1 . x)
     SwiGLU: W2 . (silu(W_gate . x) * (W_up . x)), with w1 = W_up and w3 = W_gate [R21].
     Weights are [out, in]; rows of ``xr`` are tokens.
+
+    ``h_store="bf16"`` keeps the hidden activation at the storage precision of a bf16 layer
+    between the two projections [R23]: it is rounded to the nearest bf16 (ties to even) after the
+    activation and before the down projection. Default: exact (fp64) throughout.
     """
     xr = np.asarray(xr, F64)
     up = xr @ np.asarray(w1, F64).T
@@ -270,6 +274,10 @@ def mlp(xr, w1, w3, w2, act):
         h = gelu_tanh(up)
     else:
         raise ValueError(act)
+    if h_store == "bf16":
+        h = bf16_round(h)
+    elif h_store is not None:
+        raise ValueError(h_store)
     return h @ np.asarray(w2, F64).T
 
 
@@ -287,14 +295,14 @@ def expert_kind(spec, e):
     return "const", e
 
 
-def expert_out(spec, W, layer, e, xr):
+def expert_out(spec, W, layer, e, xr, h_store=None):
     """Output of routed expert e on token rows ``xr`` [MMOE] MoE++: heavy = MLP, identity = x,
     zero = 0, constant = its learned vector v_c (independent of x [R15])."""
     kind, j = expert_kind(spec, e)
     xr = np.asarray(xr, F64)
     if kind == "heavy":
         w3 = None if W.w3[layer] is None else W.w3[layer][j]
-        return mlp(xr, W.w1[layer][j], w3, W.w2[layer][j], spec.act)
+        return mlp(xr, W.w1[layer][j], w3, W.w2[layer][j], spec.act, h_store)
     if kind == "identity":
         return xr.copy()
     if kind == "zero":
@@ -302,13 +310,13 @@ def expert_out(spec, W, layer, e, xr):
     return np.broadcast_to(np.asarray(W.const_vec[layer][j], F64), xr.shape).copy()
 
 
-def shared_out(spec, W, layer, x):
+def shared_out(spec, W, layer, x, h_store=None):
     """Sum of the always-on shared experts, weight 1 each [MMOE] (共享专家) [R19]."""
     x = np.asarray(x, F64)
     out = np.zeros_like(x)
     for i in range(spec.n_shared):
         w3 = None if W.s_w3[layer] is None else W.s_w3[layer][i]
-        out += mlp(x, W.s_w1[layer][i], w3, W.s_w2[layer][i], spec.act)
+        out += mlp(x, W.s_w1[layer][i], w3, W.s_w2[layer][i], spec.act, h_store)
     return out
 
 
@@ -358,7 +366,7 @@ def route(spec, L=None, P=None, input_probs=False, vote_dtype=F64):
 # --------------------------------------------------------------------------------------------
 
 
-def routed_part(spec, W, layer, x, rt):
+def routed_part(spec, W, layer, x, rt, h_store=None):
     """sum over a token's slots of gate weight * expert output (token / DES choice), or
     sum over the experts that picked the token of A_{s,i} * FFN_i(x_s) (expert choice;
     a token no expert picked gets 0 [R7]). [EC-DiT] 核心公式; [MMOE] MoE++."""
@@ -368,7 +376,7 @@ def routed_part(spec, W, layer, x, rt):
     if spec.mode == "ec":
         for i in range(rt["tokens"].shape[0]):
             t = rt["tokens"][i]
-            out[t] += rt["gates"][i][:, None] * expert_out(spec, W, layer, i, x[t])
+            out[t] += rt["gates"][i][:, None] * expert_out(spec, W, layer, i, x[t], h_store)
         return out
     idx, w = rt["idx"], rt["w"]
     live = ~rt["reuse"]
@@ -377,11 +385,11 @@ def routed_part(spec, W, layer, x, rt):
         if not sel.any():
             continue
         s_ids, j_ids = np.nonzero(sel)
-        out[s_ids] += w[s_ids, j_ids][:, None] * expert_out(spec, W, layer, e, x[s_ids])
+        out[s_ids] += w[s_ids, j_ids][:, None] * expert_out(spec, W, layer, e, x[s_ids], h_store)
     return out
 
 
-def layer_forward(spec, W, x, layer=0, prev_logits=None, cache=None, residual=None, rt=None):
+def layer_forward(spec, W, x, layer=0, prev_logits=None, cache=None, residual=None, rt=None, h_store=None):
     """One MoE FFN layer call.
 
     y_s = residual_s + shared(x_s) + routed_s, with routed_s from ``routed_part`` for fresh tokens
@@ -390,18 +398,19 @@ def layer_forward(spec, W, x, layer=0, prev_logits=None, cache=None, residual=No
     part is returned as the new cache.
 
     ``rt`` overrides the routing decisions (default: ``route`` on this call's logits).
+    ``h_store`` is the storage precision of the experts' hidden activations (see ``mlp``).
     Returns dict(y, logits, rt, routed, new_cache).
     """
     x = np.asarray(x, F64)
     L = router_logits(x, W.w_router[layer], prev_logits)
     if rt is None:
         rt = route(spec, L=L)
-    routed = routed_part(spec, W, layer, x, rt)
+    routed = routed_part(spec, W, layer, x, rt, h_store)
     if spec.mode != "ec" and rt["reuse"].any():
         if cache is None:
             raise ValueError("reuse needs a cache")
         routed = np.where(rt["reuse"][:, None], np.asarray(cache, F64), routed)
-    y = routed + shared_out(spec, W, layer, x)
+    y = routed + shared_out(spec, W, layer, x, h_store)
     if residual is not None:
         y = y + np.asarray(residual, F64)
     return {"y": y, "logits": L, "rt": rt, "routed": routed}
@@ -434,7 +443,7 @@ def stack_forward(spec, W, x, act_bf16=True, gate_residual=True):
     return outs
 
 
-def dice_step_loop(spec, W, xs, tau, stride, reuse_layers, act_bf16=True, rt_hook=None):
+def dice_step_loop(spec, W, xs, tau, stride, reuse_layers, act_bf16=True, rt_hook=None, h_store=None):
     """DICE denoising-step loop on one device ([DICE] 关键设计).
 
     ``xs`` are the latent tokens of the successive steps t = 0, 1, ...; each step runs the
@@ -446,10 +455,10 @@ def dice_step_loop(spec, W, xs, tau, stride, reuse_layers, act_bf16=True, rt_hoo
     recomputed (the stride refresh, and 选择性同步: layers outside ``reuse_layers`` stay
     synchronous). Fresh tokens write their routed part into the cache, rounded to the storage
     precision (bf16 for a bf16 workload); reused tokens leave it alone. The stream between layers
-    is stored in the same precision.
+    is stored in the same precision (``y``; ``y_exact`` is the layer output before that rounding).
 
-    ``rt_hook(t, layer, L, rt, spec_l)`` may replace the routing decisions of a layer call (a test
-    that accepts the other side's choice on near-ties). Returns, per step, a list of per-layer
+    ``rt_hook(t, layer, h, L, rt, spec_l)`` may replace the routing decisions of a layer call (a
+    test that accepts the other side's choice on near-ties). Returns, per step, a list of per-layer
     dicts: h_in, y, routed, cache (after the call), reuse (the mask used).
     """
     rnd = bf16_round if act_bf16 else (lambda a: np.asarray(a, F64))
@@ -464,12 +473,13 @@ def dice_step_loop(spec, W, xs, tau, stride, reuse_layers, act_bf16=True, rt_hoo
             L = router_logits(h, W.w_router[layer])
             rt = route(sp, L=L)
             if rt_hook is not None:
-                rt = rt_hook(t, layer, L, rt, sp)
-            r = layer_forward(sp, W, h, layer=layer, cache=caches[layer], residual=h, rt=rt)
+                rt = rt_hook(t, layer, h, L, rt, sp)
+            r = layer_forward(sp, W, h, layer=layer, cache=caches[layer], residual=h, rt=rt, h_store=h_store)
             caches[layer] = np.where(rt["reuse"][:, None], caches[layer], rnd(r["routed"])) \
                 if caches[layer] is not None else rnd(r["routed"])
             y = rnd(r["y"])
-            per.append({"h_in": h, "y": y, "routed": r["routed"], "cache": caches[layer], "reuse": rt["reuse"]})
+            per.append({"h_in": h, "y": y, "y_exact": r["y"], "routed": r["routed"], "cache": caches[layer],
+                        "reuse": rt["reuse"]})
             h = y
         steps.append(per)
     return steps

@@ -416,6 +416,22 @@ def test_mlp_hand_worked():
     assert abs(y[0, 0] - (2 * sig[1.0] - 6 * sig[2.0])) < 1e-12
 
 
+def test_mlp_hidden_stored_in_bf16_hand_worked():
+    """The hidden activation at its bf16 storage precision, rounded after the activation and before
+    the down projection (ties to even). x = (1, 2), W1 rows (1, 0), (-1, 0), (3, 0): z = (1, -1, 3),
+    gelu = (Phi(1), -Phi(-1), 3 Phi(3)) = (0.84134.., -0.15866.., 2.99595..), whose nearest bf16
+    numbers are 215/256, -162/1024 and 3 (the last rounds up; truncation would give 2.984375).
+    W2 = [[1, 2, 3], [0, -1, 4]] then gives exactly (9.5234375, 12.158203125)."""
+    x = np.array([[1.0, 2.0]])
+    w1 = np.array([[1.0, 0.0], [-1.0, 0.0], [3.0, 0.0]])
+    w2 = np.array([[1.0, 2.0, 3.0], [0.0, -1.0, 4.0]])
+    assert orc.mlp(x, w1, None, w2, "gelu", h_store="bf16").tolist() == [[9.5234375, 12.158203125]]
+    phi = dict((z, p) for z, p in _gold("normal_cdf.json")["values"])
+    exact = orc.mlp(x, w1, None, w2, "gelu")
+    want = [phi[1.0] - 2 * phi[-1.0] + 9 * phi[3.0], phi[-1.0] + 12 * phi[3.0]]
+    assert np.allclose(exact, [want], atol=1e-9)
+
+
 def _light_spec(**kw):
     base = dict(name="light", S=40, d=16, f=8, E_heavy=2, n_identity=1, n_zero=1, n_const=1,
                 act="gelu", mode="tc", k=1, renorm=True, dtype="f32")
