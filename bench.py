@@ -1,9 +1,11 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
-Default workload: the DiT-MoE-XL-shaped layer (32 x 256 = 8192 tokens, d=1152, 8 SwiGLU experts
-1152->4608->1152 + 2 shared experts, top-2 renormalised), bf16, seeded synthetic inputs. A step is
-one moe_layer_forward call: router GEMM, softmax + top-k, counting-sort dispatch, the grouped expert
-GEMMs (gather fused) and the combine. Inputs are resident in HBM before timing starts.
+Default workload: the largest configuration, the MMOE MoE++ stack (64 x 256 = 16384 tokens, d=1152,
+16 heavy GELU experts 1152->4608->1152 + identity, zero and constant experts + 1 shared expert, top-2
+over 19 with gate-residual routing, 4 stacked layers), bf16, seeded synthetic inputs. A step is one
+pass of the stack: per layer one moe_layer_forward call (router GEMM + the previous layer's logits,
+softmax + top-k, counting-sort dispatch, the grouped expert GEMMs with the gather fused, and the
+combine with the residual add). Inputs are resident in HBM before timing starts.
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (its duration read live with
 HIP events attached to its launches on its own stream), and the fp64 CPU oracle timed on a bounded
@@ -42,8 +44,10 @@ DESCRIPTIONS = {
     "ec_dit": "64 x 128 = 8192 tokens, d=1536, 32 GELU experts 1536->6144->1536, expert choice C=512",
     "des_vote_b025": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 16",
     "des_vote_b050": "DES-Vote decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, top-8, core 32",
-    "des_seq": "DES-Seq decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, each token its own "
-               "top-8 (experts loaded = their union)",
+    "des_seq": "DES-Seq decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, core = union of each "
+               "token's top-2, tokens re-route top-8 inside it",
+    "vanilla_top8": "vanilla decode block: 32 tokens, d=2048, 64 SwiGLU experts 2048->1024->2048, each token its own "
+                    "top-8 (experts loaded = their union)",
     "mmoe": "MMOE MoE++ stack: 64 x 256 = 16384 tokens, d=1152, 16 GELU experts + identity/zero/constant + 1 shared, "
             "top-2 with gate residual, 4 layers",
 }
@@ -54,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dit_moe_xl", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workload", default="mmoe", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
     ap.add_argument("--dice-steps", action="store_true",
@@ -94,11 +98,14 @@ def calibrate_copy():
 def des_fit(args):
     """The DES latency model ("Dynamic Expert Sharing", 2.1): an expert that serves c rows costs
     f(c) = a*c + b, b being the fetch of its weights, so a block costs a*(rows) + b*(experts used).
-    Decode blocks of N in {8, 16, 32, 64} tokens are routed by DES-Vote (core 16 and 32) and by
-    DES-Seq (each token its own top-8: the experts used are the union); the two streaming kernels'
-    time per block (HIP events on their launches) is fitted by least squares to
-    t = a*rows + b*experts + c0 (c0: the fixed cost of the two launches). Prints one JSON line per
-    block and one with the fit."""
+    Decode blocks of N in {8, 16, 32, 64} tokens are routed by vanilla top-8, DES-Vote (core 16 and
+    32) and DES-Seq (core = union of each token's top-k_seq, k_seq in {1, 2, 4}, then top-8 inside
+    it; 2.3, 3.1, 4.3); the two streaming kernels' time per block (HIP events on their launches) is
+    fitted by least squares to t = a*rows + b*experts + c0 (c0: the fixed cost of the two launches).
+    At N = 32 each DES-Seq block is also set against DES-Vote with a core of the same size, and
+    every block reports its routing fidelity against vanilla top-8 (4.4): the cosine similarity of
+    the per-expert hit counts, and the share of the vanilla top-8 routing mass the chosen experts
+    keep. Prints one JSON line per block and one with the fit."""
     import numpy as np
     import torch
 
@@ -120,42 +127,61 @@ def des_fit(args):
         copies.append((t, moe.weights_struct(t)))
     x_all = up(inp.bits["x"])
     stream = torch.cuda.current_stream()
-    rows, experts, times, lines = [], [], [], []
-    for name, spec0 in (("vote16", WORKLOADS["des_vote_b025"]), ("vote32", WORKLOADS["des_vote_b050"]),
-                        ("seq", WORKLOADS["des_seq"])):
-        for n in (8, 16, 32, 64):
-            spec = spec0.replace(S=n)
-            desc = moe.desc_from_spec(spec)
-            ws = moe.workspace(desc, device=dev)
-            rb = moe.alloc_routing(desc, device=dev)
-            x = x_all[:n].contiguous()
-            y = torch.empty_like(x)
+    rows, experts, times = [], [], []
+    vanilla_hits = {}
 
-            def call(i):
-                moe.moe_layer_forward(desc, x, copies[i % 4][1], None, None, rb.struct, None, None, y, ws,
-                                      stream=stream.cuda_stream)
+    def run_block(name, spec, n):
+        desc = moe.desc_from_spec(spec)
+        ws = moe.workspace(desc, device=dev)
+        rb = moe.alloc_routing(desc, device=dev)
+        x = x_all[:n].contiguous()
+        y = torch.empty_like(x)
 
-            for i in range(args.warmup):
-                call(i)
-            torch.cuda.synchronize()
-            moe.moe_profile_begin()
-            for i in range(args.steps):
-                call(i)
-            prof = moe.moe_profile_end()
-            torch.cuda.synchronize()
-            # per layer call (a kernel may be launched more than once per call)
-            t_us = sum(prof[k][0] * 1e3 / args.steps for k in ("stream_up", "stream_down") if k in prof)
-            layer_us = sum(v[0] * 1e3 / args.steps for v in prof.values())
-            counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
-            r, e = int(counts.sum()), int(np.count_nonzero(counts))
-            rows.append(r)
-            experts.append(e)
-            times.append(t_us)
-            line = {"block": name, "tokens": n, "rows": r, "experts": e,
-                    "weight_bytes": e * 3 * spec.d * spec.f * 2, "stream_us": round(t_us, 2),
-                    "kernels_us": round(layer_us, 2)}
-            lines.append(line)
-            print(json.dumps(line), flush=True)
+        def call(i):
+            moe.moe_layer_forward(desc, x, copies[i % 4][1], None, None, rb.struct, None, None, y, ws,
+                                  stream=stream.cuda_stream)
+
+        for i in range(args.warmup):
+            call(i)
+        torch.cuda.synchronize()
+        moe.moe_profile_begin()
+        for i in range(args.steps):
+            call(i)
+        prof = moe.moe_profile_end()
+        torch.cuda.synchronize()
+        # per layer call (a kernel may be launched more than once per call)
+        t_us = sum(prof[k][0] * 1e3 / args.steps for k in ("stream_up", "stream_down") if k in prof)
+        layer_us = sum(v[0] * 1e3 / args.steps for v in prof.values())
+        counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
+        kk = min(spec.k, spec.m_core) if spec.mode == "des" else spec.k
+        idx = rb["topk_idx"].cpu().numpy().reshape(-1)[: n * kk].reshape(n, kk)
+        probs = rb["probs"].cpu().numpy()
+        r, e = int(counts.sum()), int(np.count_nonzero(counts))
+        line = {"block": name, "tokens": n, "rows": r, "experts": e,
+                "weight_bytes": e * 3 * spec.d * spec.f * 2, "stream_us": round(t_us, 2),
+                "kernels_us": round(layer_us, 2)}
+        # routing fidelity against vanilla top-8 on the same tokens
+        hits = np.bincount(idx[idx >= 0], minlength=spec.E_heavy).astype(float)
+        if name == "vanilla":
+            vanilla_hits[n] = (hits, np.sort(probs, axis=1)[:, ::-1][:, :8].sum(1))
+        vh, vmass = vanilla_hits[n]
+        kept = np.take_along_axis(probs, np.where(idx >= 0, idx, 0), 1) * (idx >= 0)
+        line["hit_cosine_vs_vanilla"] = round(float(hits @ vh / (np.linalg.norm(hits) * np.linalg.norm(vh))), 4)
+        line["routing_mass_kept_vs_vanilla"] = round(float(np.mean(kept.sum(1) / vmass)), 4)
+        print(json.dumps(line), flush=True)
+        rows.append(r)
+        experts.append(e)
+        times.append(t_us)
+        return e
+
+    for n in (8, 16, 32, 64):
+        run_block("vanilla", WORKLOADS["vanilla_top8"].replace(S=n), n)
+        for name, spec0 in (("vote16", WORKLOADS["des_vote_b025"]), ("vote32", WORKLOADS["des_vote_b050"])):
+            run_block(name, spec0.replace(S=n), n)
+        for kq in (1, 2, 4):
+            e = run_block(f"seq_k{kq}", WORKLOADS["des_seq"].replace(S=n, vote_k=kq), n)
+            if n == 32:   # DES-Vote with a core of the same size
+                run_block(f"vote_core{e}", WORKLOADS["des_vote_b025"].replace(S=n, m_core=e), n)
     A = np.stack([np.asarray(rows, float), np.asarray(experts, float), np.ones(len(rows))], axis=1)
     coef, *_ = np.linalg.lstsq(A, np.asarray(times), rcond=None)
     pred = A @ coef
@@ -164,7 +190,7 @@ def des_fit(args):
     print(json.dumps({"fit": "stream_us = a*rows + b*experts + c0", "a_us_per_row": round(float(coef[0]), 4),
                       "b_us_per_expert": round(float(coef[1]), 4), "c0_us": round(float(coef[2]), 3),
                       "max_abs_residual_us": round(float(np.abs(pred - np.asarray(times)).max()), 3),
-                      "bytes_per_expert": bytes_per_expert,
+                      "blocks": len(rows), "bytes_per_expert": bytes_per_expert,
                       "b_as_bandwidth_GBps": round(bytes_per_expert / (float(coef[1]) * 1e-6) / 1e9, 1)}),
           flush=True)
 
@@ -431,7 +457,9 @@ def main():
     t0 = time.time()
     inp = gen_layer_inputs(spec, seed=0)
     x = up(inp.x, inp.bits.get("x"))
-    copies = 4 if spec.mode == "des" else 1      # rotate weight copies so the 256 MB MALL cannot hold them
+    # decode blocks stream their experts' weights: rotate 4 weight copies so the 256 MB MALL cannot hold them
+    streamed = bool(spec.E_heavy) and spec.S * spec.k / spec.E_heavy <= 64 and spec.mode != "ec"
+    copies = 4 if streamed else 1
     layers = []
     for layer in range(spec.n_layers):
         per_copy = []
@@ -546,7 +574,7 @@ def main():
         "stream_up": ("hbm", n_active * mats_up * f * d * (2 if spec.dtype == "bf16" else 4)),
         "stream_down": ("hbm", n_active * d * f * (2 if spec.dtype == "bf16" else 4)),
     }
-    if spec.mode == "des" or (spec.E_heavy and desc and n_rows and spec.S * spec.k / max(1, spec.E_heavy) <= 64):
+    if streamed:
         # streamed experts: the shared experts (if any) still run on the tiled GEMM
         work["gemm_up"] = ("mfma", spec.S * spec.n_shared * 2.0 * d * f * mats_up)
         work["gemm_down"] = ("mfma", spec.S * spec.n_shared * 2.0 * d * f)

@@ -5,8 +5,9 @@
  *   logits L = x . W_r^T (+ L_prev)                     router, gate residual
  *   p      = softmax(L) over the E_r routed experts      affinity
  *   routing: token choice (each token takes its top-k experts), expert choice (each expert takes
- *            its top-C tokens, C = floor(f_c * S / E_r)), or DES-Vote (a core set of M_core experts
- *            elected by summed routing weights; tokens re-route top-k inside it)
+ *            its top-C tokens, C = floor(f_c * S / E_r)), DES-Vote (a core set of M_core experts
+ *            elected by summed routing weights; tokens re-route top-k inside it) or DES-Seq (the core
+ *            is the union of every token's top-k_seq; tokens re-route top-k inside it)
  *   dispatch: tokens grouped by expert (stable counting sort)
  *   experts:  heavy = GELU or SwiGLU MLP (grouped bf16/fp32 MFMA GEMMs); identity, zero and
  *             constant experts computed inline; shared experts on every token with weight 1
@@ -18,8 +19,8 @@
  *     核心公式: token choice vs expert choice; affinity A = softmax(x' W_r); 容量因子 (capacity
  *     f_c * S / E with f_c = 2.0).
  *   "Dynamic Expert Sharing: Decoupling Memory from Parallelism in Mixture-of-Experts Diffusion
- *     LLMs": 2.1 latency model f(c) = a*c + b; 2.4 DES-Vote; 3.1 M_core = beta * M; 4.3 top-8
- *     re-activated inside the core set.
+ *     LLMs": 2.1 latency model f(c) = a*c + b; 2.3 DES-Seq; 2.4 DES-Vote; 3.1 M_core = beta * M and
+ *     the local selection count of DES-Seq; 4.3 top-8 re-activated inside the core set.
  *   "MMOE: Modernizing Diffusion Transformers with Efficient Expert Design", 方法论: MoE++ layer
  *     (heavy MLP experts, identity / zero / constant zero-computation experts), gate-residual
  *     routing, shared expert.
@@ -62,7 +63,7 @@ typedef enum {
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
 typedef enum { MOE_ACT_GELU = 0 /* erf form */, MOE_ACT_GELU_TANH = 1, MOE_ACT_SWIGLU = 2 } moe_act;
-typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1, MOE_DES_VOTE = 2 } moe_mode;
+typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1, MOE_DES_VOTE = 2, MOE_DES_SEQ = 3 } moe_mode;
 
 /* desc->flags */
 #define MOE_F_INPUT_PROBS   0x1u  /* moe_route: `logits` holds probabilities p (rows sum to 1);
@@ -87,14 +88,18 @@ typedef struct {
   int32_t k;                    /* token choice / DES re-route top-k (1 <= k <= E_r)               */
   int32_t renorm;               /* 1: chosen weights divided by their sum                          */
   float capacity_factor;        /* expert choice: C = min(S, floor(f_c * S / E_r)), C >= 1         */
-  int32_t vote_k, m_core;       /* DES: filter top-K per token, core-set size                      */
-  float reuse_tau;              /* token choice / DES: reuse cache where max_e p < tau; 0 = off    */
+  int32_t vote_k, m_core;       /* DES-Vote: filter top-K per token, core-set size;
+                                   DES-Seq: vote_k = local selection count k_seq, m_core unused     */
+  float reuse_tau;              /* token choice / DES: reuse cache where max_e p < tau; 0 = off
+                                   (DICE, 关键设计 / 条件通信)                                        */
   uint32_t flags;               /* MOE_F_*                                                         */
 } moe_desc;
 
-/* Routing results, caller-allocated device arrays. k_eff = k (token choice) or min(k, m_core) (DES);
- * R_max = S*k_eff (token choice, DES) or E_r*C (expert choice). Pointers a mode does not use may be
- * NULL. Limits: E_r <= 256, k_eff <= 16. */
+/* Routing results, caller-allocated device arrays. k_eff = k (token choice, DES-Seq) or min(k, m_core)
+ * (DES-Vote); R_max = S*k_eff (token choice, DES) or E_r*C (expert choice; S*E_r always suffices).
+ * Pointers a mode does not use may be NULL. Limits: E_r <= 256, k_eff <= 16.
+ * DES-Seq: the core's size |core| is only known on the device; a token re-routes to
+ * k' = min(k, |core|) experts and its slots k'..k-1 hold expert -1 with weight 0 and row -1. */
 typedef struct {
   int32_t *topk_idx;            /* [S,k_eff] chosen expert per slot, slots in descending key order  */
   float *topk_w;                /* [S,k_eff] gate weight per slot                                    */
@@ -107,8 +112,10 @@ typedef struct {
   int32_t *token_rows;          /* [S,k_eff] row of each slot; -1 for zero-computation experts and reused tokens */
   int32_t *token_off;           /* expert choice: [S+1] CSR offsets of each token's rows              */
   int32_t *token_list;          /* expert choice: [E_r*C] rows of each token, ascending expert        */
-  int32_t *core;                /* DES: [m_core] core experts, ascending                              */
-  float *votes;                 /* DES: [E_r] summed routing weights (fp32, tokens in ascending order) */
+  int32_t *core;                /* DES-Vote: [m_core] core experts, ascending; DES-Seq: [E_r], the
+                                   union ascending, then -1 up to E_r                                 */
+  float *votes;                 /* DES-Vote: [E_r] summed routing weights (fp32, tokens in ascending
+                                   order); DES-Seq: [E_r] tokens whose top-k_seq holds the expert      */
   uint8_t *reuse;               /* [S] 1 = token reuses its cache (nullable when reuse_tau == 0)      */
   int32_t *n_rows;              /* [1] total dispatched heavy rows R (<= R_max)                       */
   int32_t *capacity;            /* expert choice: [1] the C used                                      */
@@ -129,16 +136,24 @@ typedef struct {
 size_t moe_workspace_bytes(const moe_desc *desc /* [host] */);
 
 /* Routing from logits [S,E_r] (or probabilities with MOE_F_INPUT_PROBS): softmax, then
- *   token choice: top-k per token by (logit desc, expert asc); weights p or p / sum p (renorm);
- *   expert choice: each expert takes C tokens by (p desc, token asc); gate = p;
+ *   token choice: top-k per token by (logit desc, expert asc); weights p or p / sum p (renorm)
+ *             (EC-DiT, 三 技术架构 / 核心公式, token choice);
+ *   expert choice: each expert takes C tokens by (p desc, token asc); gate = p
+ *             (EC-DiT, 核心公式, expert choice; 容量因子: C = floor(f_c * S / E_r), clipped to S);
  *   DES-Vote: top-vote_k filter per token, votes v_e = sum_n [e in T_n] p_{n,e}, core = top m_core
- *             by (v desc, e asc), re-route top-min(k, m_core) inside the core;
+ *             by (v desc, e asc), re-route top-min(k, m_core) inside the core
+ *             (Dynamic Expert Sharing, 2.4; 3.1 M_core = beta * M; 4.3 re-activation inside the core);
+ *   DES-Seq:  core = union over tokens of each token's top-vote_k, re-route top-min(k, |core|) inside it
+ *             (Dynamic Expert Sharing, 2.3; 3.1 local selection count; 4.3);
  * then the dispatch order (counts, offsets, row_token, row_w, token_rows, token CSR), and the
- * reuse mask when reuse_tau > 0. EC-DiT 核心公式 and 容量因子; DES 2.4, 3.1, 4.3; DICE 条件通信. */
+ * reuse mask when reuse_tau > 0 (DICE, 关键设计 / 条件通信: tokens whose top score is below tau). */
 moe_status moe_route(const moe_desc *desc, const float *logits, moe_routing *routing /* [host] struct */,
                      void *ws, size_t ws_bytes, void *stream);
 
-/* x_perm[r, :] = x[row_token[r], :] for r < n_rows. x [S,d], x_perm [R_max,d]; rows >= n_rows untouched. */
+/* Dispatch: x_perm[r, :] = x[row_token[r], :] for r < n_rows. x [S,d], x_perm [R_max,d]; rows >= n_rows
+ * untouched. The tokens grouped by expert for the experts' batched MLPs: EC-DiT, 核心公式 (each expert
+ * processes the tokens routed to it); on one device DICE's all-to-all dispatch (关键设计) is this
+ * local permute. MOE_EINVAL for null pointers. */
 moe_status moe_dispatch(const moe_desc *desc, const void *x, const moe_routing *routing, void *x_perm,
                         void *stream);
 
@@ -152,19 +167,26 @@ moe_status moe_expert_ffn(const moe_desc *desc, const void *x, const void *x_per
                           const moe_weights *weights, float *y_perm, float *y_shared, void *ws, size_t ws_bytes,
                           void *stream);
 
-/* y [S,d] = residual + y_shared + routed, routed_s = sum_j topk_w[s,j] * out_j in slot order, where
- * out_j = y_perm[token_rows[s,j]] (heavy), x_s (identity), 0 (zero), const_vec[c] (constant);
- * expert choice: sum over token_list rows (ascending expert) of row_w * y_perm. fp32 accumulation,
- * one rounding to dtype. With reuse: reused tokens take routed_s = cache_s, fresh tokens write
- * cache_s = routed_s (rounded to dtype). residual, y_shared, cache are nullable. */
+/* Combine: y [S,d] = residual + y_shared + routed, routed_s = sum_j topk_w[s,j] * out_j in slot order,
+ * where out_j = y_perm[token_rows[s,j]] (heavy), x_s (identity), 0 (zero), const_vec[c] (constant),
+ * nothing for an empty DES-Seq slot (expert -1) (MMOE, 方法论: MoE++ zero-computation experts and the
+ * shared expert); expert choice: sum over token_list rows (ascending expert) of row_w * y_perm (EC-DiT,
+ * 核心公式: a token's output sums A_{s,i} FFN_i over the experts that chose it, 0 if none). fp32
+ * accumulation, one rounding to dtype. With reuse: reused tokens take routed_s = cache_s, fresh
+ * tokens write cache_s = routed_s rounded to dtype (DICE, 关键设计: 条件通信 reuses stale results for
+ * low-score tokens; 交织并行 keeps only the combine results). residual, y_shared, cache are nullable.
+ * MOE_EINVAL for a missing pointer the description needs (y_perm with heavy experts, y_shared with
+ * shared experts, const_vec with constant experts, cache and reuse with reuse_tau > 0). */
 moe_status moe_combine(const moe_desc *desc, const void *x, const moe_routing *routing, const float *y_perm,
                        const float *y_shared, const void *const_vec, void *cache, const void *residual, void *y,
                        void *stream);
 
-/* The whole layer: router GEMM (+ prev_logits, gate residual), moe_route, expert GEMMs (gather
- * fused), moe_combine. logits_out [S,E_r] fp32 (nullable) receives the final logits, the next
- * layer's prev_logits. routing may be NULL (then the workspace holds it). cache is required when
- * reuse_tau > 0. No device-to-host synchronisation. */
+/* The whole layer: router GEMM L = x . W_r^T (EC-DiT, 核心公式: scores x' W_r) plus prev_logits when
+ * given (MMOE, 方法论: gate-residual routing adds the previous layer's logits), moe_route, the expert
+ * GEMMs (gather fused), moe_combine. logits_out [S,E_r] fp32 (nullable) receives the final logits, the
+ * next layer's prev_logits. routing may be NULL (then the workspace holds it). cache is required when
+ * reuse_tau > 0 (DICE 条件通信). No device-to-host synchronisation. MOE_EINVAL with MOE_F_INPUT_PROBS
+ * (probabilities are an input of moe_route only). */
 moe_status moe_layer_forward(const moe_desc *desc, const void *x, const moe_weights *weights,
                              const float *prev_logits, float *logits_out, moe_routing *routing, void *cache,
                              const void *residual, void *y, void *ws, size_t ws_bytes, void *stream);
@@ -184,17 +206,6 @@ moe_status moe_attnres_aggregate(int32_t dtype, int32_t S, int32_t d, int32_t n,
 
 /* Static description of a status code. Thread-safe. */
 const char *moe_strerror(int status);
-
-/* Measurement helpers (not part of the layer). While profiling is on, every kernel this library
- * launches carries a start/stop hipEvent pair attached to its dispatch on its own stream, so the
- * kernel times are read on the GPU's clock. moe_profile_begin clears earlier records and turns
- * profiling on (the first 4096 launches are kept); moe_profile_end turns it off, waits for the
- * recorded launches and returns the number of distinct kernel names (or a negative moe_status);
- * moe_profile_entry reads entry i: its name (valid until the next moe_profile_begin), the summed
- * kernel time in milliseconds and the number of launches. Not thread-safe. */
-moe_status moe_profile_begin(void);
-int moe_profile_end(void);
-moe_status moe_profile_entry(int i, const char **name, double *total_ms, int32_t *launches);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,7 @@ from dataclasses import dataclass
 __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
     "MOE_BF16", "MOE_F32", "MOE_ACT_GELU", "MOE_ACT_GELU_TANH", "MOE_ACT_SWIGLU",
-    "MOE_TOKEN_CHOICE", "MOE_EXPERT_CHOICE", "MOE_DES_VOTE",
+    "MOE_TOKEN_CHOICE", "MOE_EXPERT_CHOICE", "MOE_DES_VOTE", "MOE_DES_SEQ",
     "MOE_F_INPUT_PROBS", "MOE_F_SYNC_DEBUG", "MOE_F_FORCE_TILED", "MOE_F_FORCE_STREAM", "MOE_F_ROUTE_MULTI",
     "MoeDesc", "MoeRouting", "MoeWeights", "MoeError", "MoeLibraryMissing",
     "lib", "lib_path", "EXPORTS",
@@ -24,13 +24,14 @@ __all__ = [
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_BF16, MOE_F32 = 0, 1
 MOE_ACT_GELU, MOE_ACT_GELU_TANH, MOE_ACT_SWIGLU = 0, 1, 2
-MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE, MOE_DES_VOTE = 0, 1, 2
+MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE, MOE_DES_VOTE, MOE_DES_SEQ = 0, 1, 2, 3
 MOE_F_INPUT_PROBS, MOE_F_SYNC_DEBUG, MOE_F_FORCE_TILED, MOE_F_FORCE_STREAM = 0x1, 0x4, 0x8, 0x10
 MOE_F_ROUTE_MULTI = 0x20
 
+# the layer's C ABI (include/moe.h) and the measurement hooks (include/moe_prof.h)
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_profile_entry",
-           "moe_attnres_aggregate")
+           "moe_layer_forward", "moe_strerror", "moe_attnres_aggregate")
+PROF_EXPORTS = ("moe_profile_begin", "moe_profile_end", "moe_profile_entry")
 
 _i32, _f32, _u32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p
 
@@ -208,7 +209,7 @@ def moe_profile_end() -> dict:
 # Marshalling helpers: descriptors from a layer spec, and device buffers for the routing outputs.
 
 _ACT = {"gelu": MOE_ACT_GELU, "gelu_tanh": MOE_ACT_GELU_TANH, "swiglu": MOE_ACT_SWIGLU}
-_MODE = {"tc": MOE_TOKEN_CHOICE, "ec": MOE_EXPERT_CHOICE, "des": MOE_DES_VOTE}
+_MODE = {"tc": MOE_TOKEN_CHOICE, "ec": MOE_EXPERT_CHOICE, "des": MOE_DES_VOTE, "des_seq": MOE_DES_SEQ}
 
 
 def desc_from_spec(spec, flags: int = 0) -> MoeDesc:
@@ -222,11 +223,12 @@ def desc_from_spec(spec, flags: int = 0) -> MoeDesc:
 
 @dataclass
 class RoutingBuffers:
-    """Device tensors behind a MoeRouting (allocated with torch)."""
+    """Device tensors behind a MoeRouting (allocated with torch). ``slots`` is the slot count of
+    topk_idx / topk_w / token_rows and ``rows`` the length of row_token / row_w / token_list: upper
+    bounds on what a call writes. The expert-choice capacity is read back from ``capacity``."""
 
-    k_eff: int
-    R_max: int
-    C: int
+    slots: int
+    rows: int
     tensors: dict
     struct: MoeRouting
 
@@ -234,43 +236,41 @@ class RoutingBuffers:
         return self.tensors[name]
 
 
-def routing_sizes(desc: MoeDesc) -> tuple[int, int, int]:
-    """(k_eff, R_max, C) for a descriptor, as the header defines them."""
+def routing_bounds(desc: MoeDesc) -> tuple[int, int]:
+    """(slots per token, rows) upper bounds for the routing arrays of a descriptor: k slots (DES-Vote
+    fills min(k, m_core) of them as a dense [S, min(k, m_core)] array, which fits), and S * k rows
+    (token choice, DES) or S * E_r rows (expert choice: each expert takes at most every token)."""
     E_r = desc.E_heavy + desc.n_identity + desc.n_zero + desc.n_const
     if desc.mode == MOE_EXPERT_CHOICE:
-        import math
-        C = int(min(desc.S, math.floor(float(ctypes.c_float(desc.capacity_factor).value) * desc.S / E_r)))
-        return 0, E_r * C, C
-    k_eff = min(desc.k, desc.m_core) if desc.mode == MOE_DES_VOTE else desc.k
-    return k_eff, desc.S * k_eff, 0
+        return 1, desc.S * E_r
+    return max(desc.k, 1), desc.S * max(desc.k, 1)
 
 
 def alloc_routing(desc: MoeDesc, device="cuda", with_probs: bool = True) -> RoutingBuffers:
     import torch
     E_r = desc.E_heavy + desc.n_identity + desc.n_zero + desc.n_const
-    k_eff, R_max, C = routing_sizes(desc)
+    kk, R = routing_bounds(desc)
     S = desc.S
     i32, f32 = torch.int32, torch.float32
     t = {}
-    kk = max(k_eff, 1)
     t["topk_idx"] = torch.full((S, kk), -7, dtype=i32, device=device)
     t["topk_w"] = torch.zeros((S, kk), dtype=f32, device=device)
     if with_probs:
         t["probs"] = torch.zeros((S, E_r), dtype=f32, device=device)
     t["counts"] = torch.zeros(E_r, dtype=i32, device=device)
     t["offsets"] = torch.zeros(E_r + 1, dtype=i32, device=device)
-    t["row_token"] = torch.full((max(R_max, 1),), -7, dtype=i32, device=device)
-    t["row_w"] = torch.zeros(max(R_max, 1), dtype=f32, device=device)
+    t["row_token"] = torch.full((max(R, 1),), -7, dtype=i32, device=device)
+    t["row_w"] = torch.zeros(max(R, 1), dtype=f32, device=device)
     t["token_rows"] = torch.full((S, kk), -7, dtype=i32, device=device)
     t["token_off"] = torch.zeros(S + 1, dtype=i32, device=device)
-    t["token_list"] = torch.full((max(R_max, 1),), -7, dtype=i32, device=device)
-    t["core"] = torch.full((max(desc.m_core, 1),), -7, dtype=i32, device=device)
+    t["token_list"] = torch.full((max(R, 1),), -7, dtype=i32, device=device)
+    t["core"] = torch.full((E_r,), -7, dtype=i32, device=device)
     t["votes"] = torch.zeros(E_r, dtype=f32, device=device)
     t["reuse"] = torch.zeros(S, dtype=torch.uint8, device=device)
     t["n_rows"] = torch.zeros(1, dtype=i32, device=device)
     t["capacity"] = torch.zeros(1, dtype=i32, device=device)
     st = MoeRouting(**{n: (v.data_ptr() if v is not None else None) for n, v in t.items()})
-    return RoutingBuffers(k_eff, R_max, C, t, st)
+    return RoutingBuffers(kk, R, t, st)
 
 
 def workspace(desc: MoeDesc, device="cuda"):

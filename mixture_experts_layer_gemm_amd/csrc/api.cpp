@@ -10,6 +10,7 @@
 
 #include "internal.hpp"
 #include "moe.h"
+#include "moe_prof.h"
 
 // ---------------------------------------------------------------------------------------------
 // Launch profiling: a fixed pool of events, handed out in launch order while enabled.
@@ -73,6 +74,17 @@ struct Plan {
 
 bool finite_nonneg(float v) { return std::isfinite(v) && v >= 0.f; }
 
+// Upper bound on the experts a call can route rows to: the core of DES-Vote (m_core), the union of
+// N top-k_seq sets for DES-Seq (at most S * k_seq experts), else every expert.
+int64_t max_active_experts(const moe_desc* d) {
+  const int64_t E_r = (int64_t)d->E_heavy + d->n_identity + d->n_zero + d->n_const;
+  if (d->mode == MOE_DES_VOTE) return std::min<int64_t>(d->m_core, E_r);
+  if (d->mode == MOE_DES_SEQ) return std::min<int64_t>((int64_t)d->S * d->vote_k, E_r);
+  return E_r;
+}
+
+bool is_des(const moe_desc* d) { return d->mode == MOE_DES_VOTE || d->mode == MOE_DES_SEQ; }
+
 moe_status make_plan(const moe_desc* d, Plan* p) {
   if (!d) return MOE_EINVAL;
   if (d->flags & ~kKnownFlags) return MOE_EINVAL;
@@ -81,7 +93,9 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
     return MOE_EINVAL;
   if (d->dtype != MOE_BF16 && d->dtype != MOE_F32) return MOE_EINVAL;
   if (d->act != MOE_ACT_GELU && d->act != MOE_ACT_GELU_TANH && d->act != MOE_ACT_SWIGLU) return MOE_EINVAL;
-  if (d->mode != MOE_TOKEN_CHOICE && d->mode != MOE_EXPERT_CHOICE && d->mode != MOE_DES_VOTE) return MOE_EINVAL;
+  if (d->mode != MOE_TOKEN_CHOICE && d->mode != MOE_EXPERT_CHOICE && d->mode != MOE_DES_VOTE &&
+      d->mode != MOE_DES_SEQ)
+    return MOE_EINVAL;
   const int64_t E_r = (int64_t)d->E_heavy + d->n_identity + d->n_zero + d->n_const;
   if (E_r < 1) return MOE_EINVAL;
   if ((d->E_heavy > 0 || d->n_shared > 0) && d->d_ff < 1) return MOE_EINVAL;
@@ -104,6 +118,7 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
       if (d->m_core < 1 || d->m_core > E_r || d->vote_k < 1 || d->vote_k > E_r) return MOE_EINVAL;
       p->k_eff = std::min(d->k, d->m_core);
     }
+    if (d->mode == MOE_DES_SEQ && (d->vote_k < 1 || d->vote_k > E_r)) return MOE_EINVAL;
     p->R_max = (int64_t)d->S * p->k_eff;
   }
   // What this library implements.
@@ -121,8 +136,7 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
     return MOE_EUNSUPPORTED;
   const int act = d->act;
   if (d->E_heavy > 0) {
-    const int64_t per_expert = p->R_max / std::max<int64_t>(1, std::min<int64_t>(
-                                                                   d->E_heavy, d->mode == MOE_DES_VOTE ? d->m_core : d->E_heavy));
+    const int64_t per_expert = p->R_max / std::max<int64_t>(1, std::min<int64_t>(d->E_heavy, max_active_experts(d)));
     const bool stream_ok = stream_gemm_supported(d->dtype, GEMM_UP, act, d->d_ff, d->d) &&
                            stream_gemm_supported(d->dtype, GEMM_DOWN, act, d->d, d->d_ff);
     bool stream = per_expert <= 64 && stream_ok;
@@ -156,7 +170,7 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
   };
   const int nblk = permute_num_blocks(d->S, std::max(p->k_eff, 1));
   p->o_blk = take((size_t)nblk * std::max(d->E_heavy, 1) * 4);
-  p->o_filt = take(d->mode == MOE_DES_VOTE ? S * Er * 4 : 0);
+  p->o_filt = take(is_des(d) ? S * Er * 4 : 0);
   p->o_pT = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
   p->o_tokrows = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
   p->o_tokcnt = take(d->mode == MOE_EXPERT_CHOICE ? S * 4 : 0);
@@ -177,7 +191,7 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
   p->r_trow = rt(S * k * 4);
   p->r_toff = rt((S + 1) * 4);
   p->r_tlist = rt(R * 4);
-  p->r_core = rt((size_t)std::max(d->m_core, 1) * 4);
+  p->r_core = rt((d->mode == MOE_DES_SEQ ? Er : (size_t)std::max(d->m_core, 1)) * 4);
   p->r_votes = rt(Er * 4);
   p->r_reuse = rt(S);
   p->r_nrows = rt(4);
@@ -223,7 +237,7 @@ moe_status check_routing(const moe_desc* d, const moe_routing* r) {
   } else {
     if (!r->topk_idx || !r->topk_w || !r->token_rows) return MOE_EINVAL;
     if (d->reuse_tau > 0.f && !r->reuse) return MOE_EINVAL;
-    if (d->mode == MOE_DES_VOTE && (!r->core || !r->votes)) return MOE_EINVAL;
+    if (is_des(d) && (!r->core || !r->votes)) return MOE_EINVAL;
   }
   return MOE_OK;
 }
@@ -285,7 +299,8 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
   a.n_const = d->n_const;
   a.tau = d->reuse_tau;
   a.vote_k = d->vote_k;
-  a.m_core = d->m_core;
+  a.m_core = d->mode == MOE_DES_SEQ ? 0 : d->m_core;
+  a.seq = d->mode == MOE_DES_SEQ ? 1 : 0;
   a.keys = keys;
   a.probs = r->probs;
   a.topk_idx = r->topk_idx;
@@ -293,8 +308,8 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
   a.reuse = r->reuse;
   a.votes = r->votes;
   a.core = r->core;
-  const bool des = d->mode == MOE_DES_VOTE;
-  if (des) a.k = d->k;   // the kernels apply min(k, m_core)
+  const bool des = is_des(d);
+  if (des) a.k = d->k;   // the kernels apply min(k, core size)
   PermuteArgs q{};
   q.S = d->S;
   q.k = p.k_eff;
@@ -359,8 +374,7 @@ moe_status do_experts(const moe_desc* d, const Plan& p, const void* x, const voi
     v.N = (int32_t)dm;
     v.K = (int32_t)f;
     if (p.streaming) {
-      const int max_active = (int)std::min<int64_t>(
-          {(int64_t)d->E_heavy, p.R_max, d->mode == MOE_DES_VOTE ? (int64_t)d->m_core : (int64_t)d->E_heavy});
+      const int max_active = (int)std::min<int64_t>({(int64_t)d->E_heavy, p.R_max, max_active_experts(d)});
       // Token rows per streaming pass: 64 when an expert can have more than 32 rows (a token takes an
       // expert at most once, so at most S) and the average active expert has more than 24; else 32.
       // A pass streams the expert's weights once; the wider pass costs more token-row loads.

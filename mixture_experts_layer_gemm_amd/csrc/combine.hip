@@ -91,14 +91,16 @@ __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
       float src_w[KM];
 #pragma unroll
       for (int j = 0; j < KM; ++j) {
-        src_kind[j] = 0;   // 0: nothing, 1: routed row, 2: x, 3: constant row
+        src_kind[j] = 0;   // 0: nothing (also an empty slot), 1: routed row, 2: x, 3: constant row
         src_row[j] = 0;
         src_w[j] = 0.f;
         if (j < a.k) {
-          const int e = a.topk_idx[(size_t)s * a.k + j];
+          const int e = a.topk_idx[(size_t)s * a.k + j];   // -1: an empty DES-Seq slot
           src_w[j] = a.topk_w[(size_t)s * a.k + j];
           int l = e - a.E_heavy;
-          if (l < 0) {
+          if (e < 0) {
+            // nothing
+          } else if (l < 0) {
             src_kind[j] = 1;
             src_row[j] = a.token_rows[(size_t)s * a.k + j];
           } else if (l < a.n_identity) {

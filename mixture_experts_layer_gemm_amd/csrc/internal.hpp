@@ -37,14 +37,15 @@ struct RouteArgs {
   int S, E_r, E_heavy, k, renorm, input_probs;
   int n_identity, n_zero, n_const;
   float tau;
-  int vote_k, m_core;
+  int vote_k, m_core;      // DES-Vote: filter K, core size; DES-Seq: vote_k = local count k_seq
+  int seq;                 // 1: DES-Seq (core = union of the top-vote_k sets; its size is found here)
   const float* keys;       // logits [S,E_r] or probabilities (input_probs)
   float* probs;            // [S,E_r] out (nullable)
   int32_t* topk_idx;       // [S,k]
   float* topk_w;           // [S,k]
   uint8_t* reuse;          // [S] (nullable when tau == 0)
-  float* votes;            // DES [E_r]
-  int32_t* core;           // DES [m_core]
+  float* votes;            // DES [E_r]: summed filtered probabilities (DES-Vote) or selection counts (DES-Seq)
+  int32_t* core;           // DES-Vote [m_core]; DES-Seq [E_r], the union ascending then -1
 };
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_des(const RouteArgs& a, float* ws_filt /* [S,E_r] */, hipStream_t st);
@@ -66,8 +67,9 @@ struct PermuteArgs {
 int permute_num_blocks(int S, int k);
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t st);
 
-// Token choice or DES-Vote routing plus the dispatch of PermuteArgs, in one workgroup, for small
-// calls (route_small_supported). For DES, a.k is the requested k (min(k, m_core) is applied).
+// Token choice or DES routing plus the dispatch of PermuteArgs, in one workgroup, for small calls
+// (route_small_supported). For DES, a.k is the requested k (min(k, core size) is applied); the
+// slot stride of topk_idx / topk_w / token_rows is q.k (min(k, m_core) for DES-Vote, k for DES-Seq).
 bool route_small_supported(int S, int E_r, int k);
 hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st);
 

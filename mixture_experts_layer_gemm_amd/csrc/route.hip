@@ -279,16 +279,21 @@ hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st) {
 }
 
 // =============================================================================================
-// DES-Vote, one workgroup for the whole block of N tokens (N = a.S).
-//  1. per token: probabilities, top-K filter T_n; filt[n][e] = p_{n,e} for e in T_n, else 0;
+// DES, one workgroup for the whole block of N tokens (N = a.S).
+//  1. per token: probabilities, top-K filter T_n; filt[n][e] = p_{n,e} (DES-Vote) or 1 (DES-Seq)
+//     for e in T_n, else 0;
 //  2. per expert: v_e = sum over n ascending of filt[n][e] (fp32, sequential: adding the zeros
-//     of unfiltered entries leaves the sum unchanged);
-//  3. core = the m_core experts first under (v desc, e asc), listed ascending;
-//  4. per token: top-min(k, m_core) by key among core experts; weights p or renormalised p.
+//     of unfiltered entries leaves the sum unchanged); for DES-Seq the number of tokens whose
+//     top-K holds e (exact integers);
+//  3. DES-Vote: core = the m_core experts first under (v desc, e asc); DES-Seq: core = the experts
+//     with v_e > 0 (the union of the T_n); listed ascending (DES-Seq: then -1 up to E_r);
+//  4. per token: top-min(k, |core|) by key among core experts; weights p or renormalised p; slots
+//     from min(k, |core|) up to the stride (DES-Seq only) hold expert -1 and weight 0.
 template <int LPT, int V>
 __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restrict__ filt) {
   __shared__ float s_votes[256];
   __shared__ int s_incore[256];
+  __shared__ int s_ncore;
   const int lane = threadIdx.x & 63;
   const int sub = lane & (LPT - 1);
   const int tpb = 256 / LPT;
@@ -309,7 +314,7 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
       for (int v = 0; v < V; ++v) {
         const int e = sub + v * LPT;
         if (e < E) {
-          filt[(size_t)s * E + e] = ((taken >> v) & 1u) ? p[v] : 0.f;
+          filt[(size_t)s * E + e] = ((taken >> v) & 1u) ? (a.seq ? 1.f : p[v]) : 0.f;
           if (a.probs) a.probs[(size_t)s * E + e] = p[v];
         }
       }
@@ -328,6 +333,10 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
   // 3. elect
   for (int e = threadIdx.x; e < E; e += 256) {
     const float ve = s_votes[e];
+    if (a.seq) {
+      s_incore[e] = ve > 0.f ? 1 : 0;
+      continue;
+    }
     int rank = 0;
     for (int q = 0; q < E; ++q) {
       const float vq = s_votes[q];
@@ -336,6 +345,11 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
     s_incore[e] = rank < a.m_core ? 1 : 0;
   }
   __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    for (int e = 0; e < E; ++e) n += s_incore[e];
+    s_ncore = n;
+  }
   for (int e = threadIdx.x; e < E; e += 256) {
     if (s_incore[e]) {
       int pos = 0;
@@ -343,8 +357,13 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
       a.core[pos] = e;
     }
   }
-  // 4. re-route inside the core
-  const int kk = min(a.k, a.m_core);
+  __syncthreads();
+  const int ncore = s_ncore;
+  if (a.seq)
+    for (int j = ncore + threadIdx.x; j < E; j += 256) a.core[j] = -1;
+  // 4. re-route inside the core; DES-Seq keeps the stride a.k and pads the slots past min(k, |core|)
+  const int kk = min(a.k, ncore);
+  const int ks = a.seq ? a.k : kk;
   for (int base = 0; base < a.S; base += tpb) {
     const int s = base + threadIdx.x / LPT;
     const bool live = s < a.S;
@@ -367,8 +386,12 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
         denom = t;
       }
       for (int j = 0; j < kk; ++j) {
-        a.topk_idx[(size_t)s * kk + j] = sel_e[j];
-        a.topk_w[(size_t)s * kk + j] = a.renorm ? sel_p[j] / denom : sel_p[j];
+        a.topk_idx[(size_t)s * ks + j] = sel_e[j];
+        a.topk_w[(size_t)s * ks + j] = a.renorm ? sel_p[j] / denom : sel_p[j];
+      }
+      for (int j = kk; j < ks; ++j) {
+        a.topk_idx[(size_t)s * ks + j] = -1;
+        a.topk_w[(size_t)s * ks + j] = 0.f;
       }
     }
   }
@@ -631,9 +654,10 @@ template <int LPT, int V, bool DES>
 __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, PermuteArgs q) {
   __shared__ float s_key[kSmallMaxSE];
   __shared__ float s_p[kSmallMaxSE];
-  __shared__ float s_aux[DES ? kSmallMaxSE : 1];   // DES: filtered probabilities
+  __shared__ float s_aux[DES ? kSmallMaxSE : 1];   // DES: filtered probabilities (DES-Seq: 1 per selection)
   __shared__ float s_votes[256];
   __shared__ int s_rank[256], s_core[256];
+  __shared__ int s_ncore;
   __shared__ int s_idx[kSmallMaxPairs];
   __shared__ float s_w[kSmallMaxPairs];
   __shared__ uint8_t s_reuse[kSmallMaxS];
@@ -641,8 +665,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
   __shared__ int s_cnt[256], s_off[257], s_run[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, E = a.E_r, SE = S * E;
-  const int M = a.m_core;
-  const int kk = DES ? min(a.k, M) : a.k;
+  // slot stride of the routing arrays: k (token choice, DES-Seq) or min(k, m_core) (DES-Vote); the
+  // number of slots a token fills (kk) is the same except for DES-Seq, where it is min(k, |core|)
+  // and only known after the core is formed
+  const int ks = q.k;
+  int M = a.m_core;
+  int kk = DES ? min(a.k, max(M, 1)) : a.k;
 
   for (int i = tid; i < SE; i += kSmallThreads) s_key[i] = a.keys[i];
   for (int e = tid; e < 256; e += kSmallThreads) {
@@ -672,7 +700,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     const int kq = DES ? a.vote_k : kk;   // DES: the filter; token choice: the selection
     unsigned taken;
     if constexpr (LPT == 64)
-      taken = wave_topk<V>(key, p, ~0u, E, lane, kq, (DES || !live) ? nullptr : s_idx + s * kk, s_w + s * kk);
+      taken = wave_topk<V>(key, p, ~0u, E, lane, kq, (DES || !live) ? nullptr : s_idx + s * ks, s_w + s * ks);
     else
       taken = token_topk<LPT, V>(key, p, ~0u, E, sub, lane, kq, DES ? nullptr : sel_e, sel_p);
     if (live) {
@@ -681,15 +709,15 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
         const int e = sub + v * LPT;
         if (e < E) {
           s_p[s * E + e] = p[v];
-          if constexpr (DES) s_aux[s * E + e] = ((taken >> v) & 1u) ? p[v] : 0.f;
+          if constexpr (DES) s_aux[s * E + e] = ((taken >> v) & 1u) ? (a.seq ? 1.f : p[v]) : 0.f;
         }
       }
       if (sub == 0) {
         s_reuse[s] = (a.tau > 0.f && pm < a.tau) ? 1 : 0;
         if constexpr (!DES && LPT < 64) {
           for (int j = 0; j < kk; ++j) {
-            s_idx[s * kk + j] = sel_e[j];
-            s_w[s * kk + j] = sel_p[j];
+            s_idx[s * ks + j] = sel_e[j];
+            s_w[s * ks + j] = sel_p[j];
           }
         }
       }
@@ -711,11 +739,12 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       a.votes[e] = v;
     }
     lds_barrier();
-    // core: the M experts of largest vote (ties to the lower index). Expert e's rank is the number
-    // of experts before it in that order; the E x E comparisons are split over all threads (each
-    // expert gets kSmallThreads / E of them, adding partial counts into s_rank, zero from the start),
-    // and the core is then listed ascending by a prefix count over the membership flags.
-    {
+    // core: DES-Vote: the M experts of largest vote (ties to the lower index). Expert e's rank is
+    // the number of experts before it in that order; the E x E comparisons are split over all
+    // threads (each expert gets kSmallThreads / E of them, adding partial counts into s_rank, zero
+    // from the start). DES-Seq: the experts some token selected (vote > 0). The core is then
+    // listed ascending by a prefix count over the membership flags.
+    if (!a.seq) {
       const int per = max(1, kSmallThreads / E);   // threads per expert
       const int span = (E + per - 1) / per;        // rivals per thread
       for (int t = tid; t < E * per; t += kSmallThreads) {
@@ -735,7 +764,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       int cbase = 0;
       for (int e0 = 0; e0 < E; e0 += 64) {
         const int e = e0 + lane;
-        const bool in = e < E && s_rank[e] < M;
+        const bool in = e < E && (a.seq ? s_votes[e] > 0.f : s_rank[e] < M);
         const uint64_t m = __ballot(in);
         if (in) {
           const int pos = cbase + __popcll(m & lanemask_lt());
@@ -744,8 +773,13 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
         }
         cbase += __popcll(m);
       }
+      if (a.seq)
+        for (int j = cbase + lane; j < E; j += 64) a.core[j] = -1;
+      if (lane == 0) s_ncore = cbase;
     }
     lds_barrier();
+    M = s_ncore;
+    kk = min(a.k, M);
     // selection: the top kk of each token inside the core. The keys of each token's core experts
     // are first gathered as order-preserving integers (s_aux, free again); lane (token s, core slot
     // c) then ranks its expert among them (key descending; the core is ascending, so ties go to the
@@ -768,33 +802,40 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       }
       if (r < kk) {
         const int ec = s_core[c];
-        s_idx[s * kk + r] = ec;
-        s_w[s * kk + r] = s_p[s * E + ec];
+        s_idx[s * ks + r] = ec;
+        s_w[s * ks + r] = s_p[s * E + ec];
       }
     }
     lds_barrier();
   }
-  // weights: p, or p over the sum of the chosen p in slot order
+  // weights: p, or p over the sum of the chosen p in slot order; DES-Seq slots past min(k, |core|)
+  // hold expert -1 and weight 0
   for (int s = tid; s < S; s += kSmallThreads) {
     float denom = 1.f;
     if (a.renorm) {
       float t = 0.f;
 #pragma unroll 4
-      for (int j = 0; j < kk; ++j) t += s_w[s * kk + j];
+      for (int j = 0; j < kk; ++j) t += s_w[s * ks + j];
       denom = t;
     }
 #pragma unroll 4
     for (int j = 0; j < kk; ++j) {
-      const float wj = a.renorm ? s_w[s * kk + j] / denom : s_w[s * kk + j];
-      s_w[s * kk + j] = wj;
-      a.topk_idx[(size_t)s * kk + j] = s_idx[s * kk + j];
-      a.topk_w[(size_t)s * kk + j] = wj;
+      const float wj = a.renorm ? s_w[s * ks + j] / denom : s_w[s * ks + j];
+      s_w[s * ks + j] = wj;
+      a.topk_idx[(size_t)s * ks + j] = s_idx[s * ks + j];
+      a.topk_w[(size_t)s * ks + j] = wj;
+    }
+    for (int j = kk; j < ks; ++j) {
+      s_idx[s * ks + j] = -1;
+      s_w[s * ks + j] = 0.f;
+      a.topk_idx[(size_t)s * ks + j] = -1;
+      a.topk_w[(size_t)s * ks + j] = 0.f;
     }
   }
   lds_barrier();
 
-  // dispatch: pair p = s * kk + j goes to a row when its expert is heavy and s does not reuse
-  const int P = S * kk;
+  // dispatch: pair p = s * ks + j goes to a row when its expert is heavy and s does not reuse
+  const int P = S * ks;
   const bool use_reuse = q.reuse != nullptr;
   auto live_pair = [&](int p, int& e) -> bool {
     if (p >= P) {
@@ -802,7 +843,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       return false;
     }
     e = s_idx[p];
-    return e >= 0 && e < q.E_heavy && !(use_reuse && s_reuse[p / kk]);
+    return e >= 0 && e < q.E_heavy && !(use_reuse && s_reuse[p / ks]);
   };
   for (int p = tid; p < P; p += kSmallThreads) {
     int e;
@@ -855,7 +896,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       int base = s_off[e] + s_run[e];
       for (int o = 0; o < wave; ++o) base += s_wcnt[o][e];
       const int row = base + __popcll(lower);
-      q.row_token[row] = p / kk;
+      q.row_token[row] = p / ks;
       q.row_w[row] = s_w[p];
       q.token_rows[p] = row;
     } else if (p < P) {
@@ -886,8 +927,8 @@ static void route_small_t(const RouteArgs& a, const PermuteArgs& q, bool des, hi
 }
 
 hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st) {
-  const int kk = des ? std::min(a.k, a.m_core) : a.k;
-  if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > 256) return hipErrorInvalidValue;
+  const int kk = des ? (a.seq ? a.k : std::min(a.k, a.m_core)) : a.k;
+  if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > 256 || q.k != kk) return hipErrorInvalidValue;
   const int E = a.E_r;
   if (E <= 8) route_small_t<8, 1>(a, q, des, st);
   else if (E <= 16) route_small_t<16, 1>(a, q, des, st);

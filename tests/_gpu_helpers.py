@@ -31,6 +31,22 @@ def dev_tensor(vals: np.ndarray, bits, dtype: str, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(vals, np.float32)).to(device)
 
 
+def slots(spec) -> int:
+    """Slots per token that the library fills densely: min(k, m_core) for DES-Vote, else k."""
+    return min(spec.k, spec.m_core) if spec.mode == "des" else spec.k
+
+
+def routing_np(rb, spec) -> dict:
+    """Host copies of the routing buffers, with the per-slot arrays viewed as [S, slots]."""
+    g = {k: v.cpu().numpy() for k, v in rb.tensors.items()}
+    if spec.mode == "ec":
+        return g
+    ks = slots(spec)
+    for name in ("topk_idx", "topk_w", "token_rows"):
+        g[name] = g[name].reshape(-1)[: spec.S * ks].reshape(spec.S, ks)
+    return g
+
+
 def to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)
@@ -76,39 +92,61 @@ def run_layer(spec, x_dev, wt, flags=0, prev=None, cache=None, residual=None, ws
     return y, logits, routing
 
 
-def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what="", base_gpu=None, base_ref=None):
-    """Layer-output tolerance. With base_gpu/base_ref (the residual each side added), the max-abs
-    bound applies to the layer's increment y - base, plus the bf16 half-ulp of the stored sum
-    (<= 2^-8 |y|): a residual output of magnitude 8 already carries a rounding of up to 0.016, and
-    each side's residual input is its own bf16 stream."""
+def bf16_half_ulp(a: np.ndarray) -> np.ndarray:
+    """Half the spacing of bfloat16 numbers at |a| (8 significant bits): 2^(e - 8) for
+    2^e <= |a| < 2^(e+1); 0 at a = 0."""
+    a = np.abs(np.asarray(a, np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 8), 0.0)
+
+
+def assert_close(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str, what=""):
+    """Layer-output tolerance against the fp64 oracle.
+
+    bf16: rel-L2 <= 5e-3 and max-abs <= 2e-2. The output is stored in bf16, so it carries up to
+    half a bf16 ulp of rounding that no implementation can avoid; the max-abs bound applies to the
+    value before that rounding, i.e. |y_gpu - y_ref| - half_ulp(max(|y_gpu|, |y_ref|)) <= 2e-2.
+    fp32: rel-L2 <= 1e-5 and max-abs <= 1e-5 * max |y_ref|. Prints the measured values and the
+    margin (bound / measured) of each bound."""
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
     assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
-    diff = y_gpu - y_ref
-    nref = np.linalg.norm(y_ref)
-    rel = np.linalg.norm(diff) / max(nref, 1e-30)
-    allow = 0.0
-    scale = 1.0
-    if base_gpu is not None:
-        inc_ref = y_ref - np.asarray(base_ref, np.float64)
-        diff = (y_gpu - np.asarray(base_gpu, np.float64)) - inc_ref
-        allow = 2.0 ** -8 * np.abs(y_ref)
-        # the absolute bound is for unit-RMS layer outputs; deeper stack layers add larger increments
-        scale = max(1.0, float(np.sqrt(np.mean(inc_ref ** 2))))
-    excess = np.abs(diff) - allow
-    mx = excess.max() if diff.size else 0.0
+    diff = np.abs(y_gpu - y_ref)
+    rel = np.linalg.norm(diff) / max(np.linalg.norm(y_ref), 1e-30)
+    raw = float(diff.max()) if diff.size else 0.0
     if dtype == "bf16":
-        tag = "max-abs" if base_gpu is None else "max-abs of increment beyond half-ulp"
-        say(f"  {what}: rel-L2 {rel:.3e} (<= {BF16_REL_L2}), {tag} {mx:.3e} (<= {BF16_MAX_ABS} x {scale:.2f})")
+        excess = diff - bf16_half_ulp(np.maximum(np.abs(y_gpu), np.abs(y_ref)))
+        mx = max(0.0, float(excess.max())) if diff.size else 0.0
+        say(f"  {what}: rel-L2 {rel:.3e} (<= {BF16_REL_L2}, margin {BF16_REL_L2 / max(rel, 1e-30):.1f}x), "
+            f"max-abs {raw:.3e}, beyond the output's half-ulp {mx:.3e} (<= {BF16_MAX_ABS}, "
+            f"margin {BF16_MAX_ABS / max(mx, 1e-30):.1f}x), n={y_ref.size}")
         assert rel <= BF16_REL_L2, f"{what}: rel-L2 {rel}"
-        assert mx <= BF16_MAX_ABS * scale, f"{what}: max-abs {mx}"
+        assert mx <= BF16_MAX_ABS, f"{what}: max-abs beyond half-ulp {mx}"
     else:
-        mx = np.abs(diff).max() if diff.size else 0.0
-        scale = max(np.abs(y_ref).max(), 1e-30)
-        say(f"  {what}: rel-L2 {rel:.3e}, max-abs/max|y| {mx / scale:.3e} (<= {F32_REL})")
+        scale = max(float(np.abs(y_ref).max()) if y_ref.size else 0.0, 1e-30)
+        say(f"  {what}: rel-L2 {rel:.3e} (<= {F32_REL}, margin {F32_REL / max(rel, 1e-30):.1f}x), "
+            f"max-abs/max|y| {raw / scale:.3e} (<= {F32_REL}, margin {F32_REL * scale / max(raw, 1e-30):.1f}x)")
         assert rel <= F32_REL, f"{what}: rel-L2 {rel}"
-        assert mx <= F32_REL * scale, f"{what}: max-abs {mx}"
+        assert raw <= F32_REL * scale, f"{what}: max-abs {raw}"
+
+
+def h_store(spec):
+    """Storage precision of the hidden activation between the two projections: the layer dtype
+    (bf16 layers keep H in bf16; fp32 layers keep it exact to fp32)."""
+    return "bf16" if spec.dtype == "bf16" else None
+
+
+def assert_rel_exact(y_gpu: np.ndarray, y_exact: np.ndarray, what=""):
+    """The relative bound against the oracle with exact (fp64) hidden activations: the layer's bf16
+    storage of H is the only intermediate rounding that comparison does not model, and it stays
+    within rel-L2 5e-3."""
+    y_gpu = np.asarray(y_gpu, np.float64)
+    y_exact = np.asarray(y_exact, np.float64)
+    rel = np.linalg.norm(y_gpu - y_exact) / max(np.linalg.norm(y_exact), 1e-30)
+    say(f"  {what} vs exact-H oracle: rel-L2 {rel:.3e} (<= {BF16_REL_L2}, margin {BF16_REL_L2 / max(rel, 1e-30):.1f}x), "
+        f"max-abs {np.abs(y_gpu - y_exact).max() if y_gpu.size else 0.0:.3e} (information)")
+    assert rel <= BF16_REL_L2, f"{what}: rel-L2 vs exact-H oracle {rel}"
 
 
 # ------------------------------------------------------------------------------------------------
@@ -125,7 +163,7 @@ def reconcile_tc(spec, L64, rt, idx_gpu, reuse_gpu=None, eps=1e-4, max_frac=1e-3
     P = rt["P"]
     k = idx_gpu.shape[1]
     keys = L64
-    if spec.mode == "des":
+    if spec.mode in ("des", "des_seq"):
         core = rt["core"]
         mask = np.full(L64.shape, -np.inf)
         mask[:, core] = 0.0
@@ -211,4 +249,27 @@ def reconcile_des(spec, rt, core_gpu, L64, eps=1e-5):
     idx, w = orc.core_reroute(L64, P, core_gpu, spec.k, spec.renorm)
     rt["idx"], rt["w"] = idx, w
     say("  near-tie DES core reconciled")
+    return rt
+
+
+def reconcile_des_seq(spec, rt, core_gpu, L64, eps=1e-4):
+    """DES-Seq: the core is the union of each token's top-k_seq. An expert may be in one side's core
+    and not the other's only through a near tie at some token's k_seq boundary; then the GPU's core
+    is taken and the oracle re-routes inside it."""
+    core_gpu = np.asarray(core_gpu, np.int64)
+    core_gpu = np.sort(core_gpu[core_gpu >= 0])
+    if np.array_equal(core_gpu, rt["core"]):
+        return rt
+    kq = spec.vote_k
+    srt = -np.sort(-L64, axis=1)
+    kth = srt[:, kq - 1]
+    nxt = srt[:, kq] if L64.shape[1] > kq else np.full(L64.shape[0], -np.inf)
+    for e in set(core_gpu.tolist()) ^ set(rt["core"].tolist()):
+        near = (np.abs(L64[:, e] - kth) < eps) & (kth - nxt < eps)
+        assert near.any(), f"DES-Seq core differs at expert {e} without a near tie"
+    rt = dict(rt)
+    rt["core"] = core_gpu
+    idx, w = orc.core_reroute(L64, rt["P"], core_gpu, spec.k, spec.renorm)
+    rt["idx"], rt["w"] = idx, w
+    say("  near-tie DES-Seq core reconciled")
     return rt

@@ -3,6 +3,7 @@ declares, and rejects bad arguments with the documented status before any launch
 import ctypes
 import os
 import re
+import subprocess
 
 import pytest
 
@@ -21,17 +22,30 @@ def built_library():
     moe.lib()
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+def _declared(header="moe.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     return set(re.findall(r"^\s*(?:const\s+char\s*\*\s*|size_t\s+|moe_status\s+|int\s+)(moe_\w+)\s*\(", src, flags=re.M))
 
 
-def test_exports_every_declared_entry_point():
-    names = _declared()
-    assert names == set(moe.EXPORTS)
+# The layer's boundary: the five calls of the hot path, the two helpers, and the MMOE block-level
+# aggregation next to the layer.
+LAYER_ABI = {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+             "moe_workspace_bytes", "moe_strerror", "moe_attnres_aggregate"}
+
+
+def _exported():
+    """moe_* functions the shared library exports (its dynamic symbol table)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path()], capture_output=True, text=True, check=True)
+    return {ln.split()[-1] for ln in out.stdout.splitlines() if ln.split() and ln.split()[-1].startswith("moe_")}
+
+
+def test_exports_exactly_the_declared_entry_points():
+    assert _declared("moe.h") == LAYER_ABI == set(moe.EXPORTS)
+    assert _declared("moe_prof.h") == set(moe.PROF_EXPORTS)
     L = ctypes.CDLL(moe.lib_path())
-    for n in names:
+    for n in LAYER_ABI | set(moe.PROF_EXPORTS):
         assert hasattr(L, n), n
+    assert _exported() == LAYER_ABI | set(moe.PROF_EXPORTS)
 
 
 def test_strerror():
@@ -55,11 +69,12 @@ def _desc(**kw):
 
 
 INVALID = [
-    dict(k=0), dict(k=9), dict(S=0), dict(d=0), dict(E_heavy=-1), dict(dtype=7), dict(act=5), dict(mode=3),
+    dict(k=0), dict(k=9), dict(S=0), dict(d=0), dict(E_heavy=-1), dict(dtype=7), dict(act=5), dict(mode=4),
     dict(d_ff=0), dict(reuse_tau=-0.5), dict(reuse_tau=float("nan")), dict(flags=0x1000),
     dict(flags=moe.MOE_F_FORCE_TILED | moe.MOE_F_FORCE_STREAM),
     dict(mode=moe.MOE_DES_VOTE, m_core=0, vote_k=8), dict(mode=moe.MOE_DES_VOTE, m_core=9, vote_k=2),
     dict(mode=moe.MOE_DES_VOTE, m_core=4, vote_k=0),
+    dict(mode=moe.MOE_DES_SEQ, vote_k=0), dict(mode=moe.MOE_DES_SEQ, vote_k=9),
     dict(mode=moe.MOE_EXPERT_CHOICE, capacity_factor=0.0),
     dict(mode=moe.MOE_EXPERT_CHOICE, capacity_factor=0.0009),            # C rounds to 0
     dict(E_heavy=0, n_identity=0, n_zero=0, n_const=0),

@@ -1,27 +1,35 @@
 """GPU parity of the whole layer (moe_layer_forward and the four-call path) against the fp64 oracle,
-on every workload shape: reduced token counts that span several tiles with ragged tails, and the
-full sizes on sampled tokens."""
+on every workload shape: reduced token counts that span several tiles with ragged tails, and every
+token of every workload at its full size, in the launch configuration the benchmark uses."""
 import numpy as np
 import pytest
 import torch
 
 import mixture_experts_layer_gemm_amd as moe
 import oracle as orc
-from _gpu_helpers import (assert_close, dev_tensor, reconcile_des, reconcile_ec, reconcile_tc, run_layer, say,
-                          to_np, torch_dtype, upload_layer)
+from _gpu_helpers import (assert_close, assert_rel_exact, dev_tensor, h_store, reconcile_des, reconcile_des_seq,
+                          reconcile_ec, reconcile_tc, routing_np, run_layer, say, to_np, upload_layer)
 from synth import WORKLOADS, gen_layer_inputs, gen_tensor
 
 pytestmark = pytest.mark.gpu
 
 
 def _oracle_rt(spec, L64, got_rb, reuse=True, eps=1e-4, max_frac=1e-3):
+    """The oracle's routing of L64, with near-tie decisions taken from the GPU where both are valid."""
     rt = orc.route(spec, L=L64)
-    g = {k: v.cpu().numpy() for k, v in got_rb.tensors.items()}
+    g = routing_np(got_rb, spec)
     if spec.mode == "ec":
         return reconcile_ec(spec, rt, g["row_token"], rt["C"])
     if spec.mode == "des":
         rt = reconcile_des(spec, rt, g["core"][: spec.m_core], L64)
-    return reconcile_tc(spec, L64, rt, g["topk_idx"], g["reuse"] if (reuse and spec.reuse_tau > 0) else None,
+    idx_gpu = g["topk_idx"]
+    if spec.mode == "des_seq":
+        rt = reconcile_des_seq(spec, rt, g["core"], L64)
+        kp = rt["idx"].shape[1]                      # min(k, |core|); the rest are empty slots
+        assert np.all(idx_gpu[:, kp:] == -1) and np.all(g["topk_w"][:, kp:] == 0)
+        assert np.all(g["token_rows"][:, kp:] == -1)
+        idx_gpu = idx_gpu[:, :kp]
+    return reconcile_tc(spec, L64, rt, idx_gpu, g["reuse"] if (reuse and spec.reuse_tau > 0) else None,
                         eps=eps, max_frac=max_frac)
 
 
@@ -41,16 +49,19 @@ def _layer_case(spec, seed=0, flags=0, with_cache=False, residual=False):
     L64 = orc.router_logits(inp.x, inp.w_router[0])
     assert np.allclose(to_np(logits), L64, atol=2e-5 * max(1.0, np.abs(L64).max()))
     rt = _oracle_rt(spec, L64, rb)
-    ref = orc.layer_forward(spec, inp, inp.x, cache=cache_np, rt=rt, residual=inp.x if residual else None)
-    base = inp.x if residual else None
-    assert_close(to_np(y), ref["y"], spec.dtype, spec.name, base_gpu=base, base_ref=base)
+    res_np = inp.x if residual else None
+    ref = orc.layer_forward(spec, inp, inp.x, cache=cache_np, rt=rt, residual=res_np, h_store=h_store(spec))
+    assert_close(to_np(y), ref["y"], spec.dtype, spec.name)
+    if h_store(spec):
+        exact = orc.layer_forward(spec, inp, inp.x, cache=cache_np, rt=rt, residual=res_np)
+        assert_rel_exact(to_np(y), exact["y"], spec.name)
     if with_cache:
         # fresh tokens wrote their routed part to the cache; reused tokens left it alone
         fresh = ~rt["reuse"]
         got_cache = to_np(cache)
         assert np.array_equal(got_cache[rt["reuse"]], cache_np[rt["reuse"]])
         assert_close(got_cache[fresh], ref["routed"][fresh], spec.dtype, spec.name + " cache")
-    return inp, rt, y
+    return inp, rt, y, rb
 
 
 def test_tiny_f32_layer_full_size():
@@ -68,7 +79,7 @@ def test_dit_moe_xl_layer_reduced():
 
 def test_dit_moe_xl_reuse_layer_reduced():
     spec = WORKLOADS["dit_moe_xl_reuse"].replace(S=900)
-    _, rt, _ = _layer_case(spec, with_cache=True)
+    _, rt, _, _ = _layer_case(spec, with_cache=True)
     assert 0 < rt["reuse"].sum() < spec.S
 
 
@@ -80,7 +91,7 @@ def test_reuse_extremes():
 
 def test_ec_dit_layer_reduced():
     spec = WORKLOADS["ec_dit"].replace(S=1024)
-    _, rt, _ = _layer_case(spec)
+    _, rt, _, _ = _layer_case(spec)
     assert rt["C"] == 64
 
 
@@ -91,25 +102,44 @@ def test_des_layer_full_size(name):
     _layer_case(spec, flags=moe.MOE_F_FORCE_TILED)
 
 
-def test_des_seq_layer_full_size():
-    """DES-Seq ("Dynamic Expert Sharing", 2.3): each token of the block keeps its own top-8 and the
-    experts streamed are their union. Layer parity, and the streamed set equals the oracle's
-    DES-Seq core of the (reconciled) routing."""
-    spec = WORKLOADS["des_seq"]
-    inp, rt, _ = _layer_case(spec)
-    inp2 = gen_layer_inputs(spec, seed=0)
-    x = dev_tensor(inp2.x, inp2.bits.get("x"), spec.dtype)
-    _, logits, rb = run_layer(spec, x, upload_layer(inp2))
+def test_vanilla_top8_block_full_size():
+    """The vanilla decode block the DES variants are measured against: each token its own top-8; the
+    experts streamed are the union of the tokens' choices."""
+    spec = WORKLOADS["vanilla_top8"]
+    inp, rt, _, rb = _layer_case(spec)
     counts = rb["counts"].cpu().numpy()[: spec.E_heavy]
-    active = np.flatnonzero(counts > 0)
-    L64 = orc.router_logits(inp2.x, inp2.w_router[0])
-    rt2 = _oracle_rt(spec, L64, rb)
-    assert np.array_equal(active, np.unique(rt2["idx"]))
-    # without near-ties the reconciled routing is the oracle's own, and so is the union
-    core = orc.des_seq_core(L64, spec.k)
-    if np.array_equal(rt2["idx"], orc.route(spec, L=L64)["idx"]):
-        assert np.array_equal(active, core)
+    assert np.array_equal(np.flatnonzero(counts > 0), np.unique(rt["idx"]))
     assert counts.sum() == spec.S * spec.k
+
+
+@pytest.mark.parametrize("k_seq", [1, 2, 4])
+def test_des_seq_block_full_size(k_seq):
+    """DES-Seq ("Dynamic Expert Sharing", 2.3, 3.1, 4.3): the core is the union of the tokens' top-k_seq
+    and every token re-activates its top-8 inside it. The core and votes (selection counts) match the
+    oracle, only core experts get rows, and the layer output matches; streamed and tiled paths."""
+    spec = WORKLOADS["des_seq"].replace(vote_k=k_seq)
+    for flags in (0, moe.MOE_F_FORCE_TILED):
+        inp, rt, _, rb = _layer_case(spec, flags=flags)
+        g = routing_np(rb, spec)
+        core = g["core"]
+        n = int(np.count_nonzero(core >= 0))
+        assert np.array_equal(core[:n], rt["core"]) and np.all(core[n:] == -1)
+        L64 = orc.router_logits(inp.x, inp.w_router[0])
+        if np.array_equal(rt["core"], orc.route(spec, L=L64)["core"]):
+            assert np.array_equal(g["votes"], orc.des_seq_counts(L64, k_seq, spec.E_routed).astype(np.float32))
+        counts = g["counts"][: spec.E_heavy]
+        assert set(np.flatnonzero(counts > 0)) <= set(rt["core"].tolist())
+        assert counts.sum() == spec.S * min(spec.k, n)
+
+
+def test_des_seq_core_smaller_than_k():
+    """A 3-token block with k_seq = 1 and k = 8: the core holds at most 3 experts, so every token keeps
+    all of them and its other slots are empty (expert -1, weight 0)."""
+    spec = WORKLOADS["des_seq"].replace(S=3, vote_k=1, d=256, f=256)
+    _, rt, _, rb = _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
+    g = routing_np(rb, spec)
+    n = rt["core"].size
+    assert n <= 3 and np.all(g["topk_idx"][:, n:] == -1) and np.all(g["topk_w"][:, n:] == 0)
 
 
 @pytest.mark.parametrize("d,f,act,S,m_core", [
@@ -141,33 +171,33 @@ def test_single_expert_layer_is_a_dense_mlp(mode):
     the layer is a dense MLP over the tokens in order, the shape of bench.py --dense."""
     base = WORKLOADS["dit_moe_xl"] if mode == "tc" else WORKLOADS["ec_dit"]
     spec = base.replace(S=700, E_heavy=1, n_shared=0, k=1)
-    _, rt, _ = _layer_case(spec)
+    _, rt, _, _ = _layer_case(spec)
     if mode == "ec":
         assert rt["C"] == spec.S
 
 
 def test_light_experts_only_layer():
     """No heavy experts: identity, zero and constant experts plus a shared expert."""
-    spec = WORKLOADS["mmoe"].replace(S=500, d=256, f=512, E_heavy=0)
+    spec = WORKLOADS["mmoe"].replace(S=500, d=256, f=512, E_heavy=0, n_layers=1)
     _layer_case(spec)
 
 
 def test_identity_only_is_exact():
     spec = WORKLOADS["mmoe"].replace(S=333, d=256, f=512, E_heavy=0, n_identity=1, n_zero=0, n_const=0,
-                                     n_shared=0, k=1)
+                                     n_shared=0, k=1, n_layers=1)
     inp = gen_layer_inputs(spec)
     x = dev_tensor(inp.x, inp.bits["x"], "bf16")
     y, _, _ = run_layer(spec, x, upload_layer(inp))
     assert torch.equal(y, x)
 
 
-def test_mmoe_stack_reduced():
-    """Four MoE++ layers with gate residual on a residual stream.
+def _stack_case(spec, end_to_end=True):
+    """Stacked MoE++ layers with gate residual on a residual stream, each layer in the benchmark's
+    launch configuration (one moe_layer_forward with the residual fused into the combine).
 
     Per layer, both sides start from the same inputs: the oracle's bf16 stream h_l and its logits
     L_{l-1} rounded to fp32 go to the GPU layer, so each layer is checked on its own. Then the GPU
     runs the whole stack on its own outputs and the final stream is compared end to end."""
-    spec = WORKLOADS["mmoe"].replace(S=600)
     say(f"stack {spec.name}: S={spec.S} layers={spec.n_layers}")
     inp = gen_layer_inputs(spec)
     h64 = inp.x.astype(np.float64)
@@ -188,11 +218,15 @@ def test_mmoe_stack_reduced():
         L64 = orc.router_logits(h64, inp.w_router[layer], prev64)
         assert np.allclose(to_np(logits), L64, atol=2e-5 * max(1.0, np.abs(L64).max()))
         rt = _oracle_rt(spec, L64, rb)
-        ref = orc.layer_forward(spec, inp, h64, layer=layer, prev_logits=prev64, residual=h64, rt=rt)
-        assert_close(to_np(y), ref["y"], "bf16", f"layer {layer}", base_gpu=h64, base_ref=h64)
+        ref = orc.layer_forward(spec, inp, h64, layer=layer, prev_logits=prev64, residual=h64, rt=rt, h_store="bf16")
+        assert_close(to_np(y), ref["y"], "bf16", f"layer {layer}")
+        exact = orc.layer_forward(spec, inp, h64, layer=layer, prev_logits=prev64, residual=h64, rt=rt)
+        assert_rel_exact(to_np(y), exact["y"], f"layer {layer}")
         h64 = orc.bf16_round(ref["y"])
         prev32 = ref["logits"].astype(np.float32)
-    # end to end on the GPU's own stream
+        del rb, y, logits, h_dev, prev_dev
+    if not end_to_end:
+        return
     h_dev = dev_tensor(inp.x, inp.bits["x"], "bf16")
     prev_dev = None
     for layer in range(spec.n_layers):
@@ -209,6 +243,10 @@ def test_mmoe_stack_reduced():
     assert rel <= 5e-2
 
 
+def test_mmoe_stack_reduced():
+    _stack_case(WORKLOADS["mmoe"].replace(S=600))
+
+
 def test_four_call_path_matches_layer_forward():
     """moe_route + moe_dispatch + moe_expert_ffn + moe_combine == moe_layer_forward (bitwise)."""
     spec = WORKLOADS["dit_moe_xl"].replace(S=513)
@@ -220,9 +258,9 @@ def test_four_call_path_matches_layer_forward():
     rb = moe.alloc_routing(desc)
     ws = moe.workspace(desc)
     moe.moe_route(desc, logits, rb.struct, ws)
-    xp = torch.empty((rb.R_max, spec.d), dtype=torch.bfloat16, device="cuda")
+    xp = torch.empty((rb.rows, spec.d), dtype=torch.bfloat16, device="cuda")
     moe.moe_dispatch(desc, x, rb.struct, xp)
-    yp = torch.empty((rb.R_max, spec.d), dtype=torch.float32, device="cuda")
+    yp = torch.empty((rb.rows, spec.d), dtype=torch.float32, device="cuda")
     ys = torch.empty((spec.S, spec.d), dtype=torch.float32, device="cuda")
     w = moe.weights_struct(wt)
     moe.moe_expert_ffn(desc, x, xp, rb.struct, w, yp, ys, ws)
@@ -236,71 +274,40 @@ def test_four_call_path_matches_layer_forward():
 
 
 # ------------------------------------------------------------------------------------------------
-# Full sizes, in the launch configuration the benchmark uses, checked on sampled tokens.
+# Full sizes, every token, in the launch configuration the benchmark uses.
 
-def _sampled_tc_check(spec, seed=0, n_sample=48):
-    inp = gen_layer_inputs(spec, seed=seed)
-    x = dev_tensor(inp.x, inp.bits["x"], spec.dtype)
-    wt = upload_layer(inp)
-    cache_np = cache = None
-    if spec.reuse_tau > 0:
-        cv, cb = gen_tensor(np.random.default_rng(seed + 100), (spec.S, spec.d), 0.5, spec.dtype)
-        cache_np, cache = cv.astype(np.float64), dev_tensor(cv, cb, spec.dtype)
-    y, logits, rb = run_layer(spec, x, wt, cache=cache)
-    rng = np.random.default_rng(seed + 7)
-    sample = np.sort(rng.choice(spec.S, size=n_sample, replace=False))
-    sample[-1] = spec.S - 1
-    xs = inp.x[sample].astype(np.float64)
-    L64 = orc.router_logits(xs, inp.w_router[0])
-    rt = orc.route(spec, L=L64)
-    g_idx = rb["topk_idx"].cpu().numpy()[sample]
-    g_reuse = rb["reuse"].cpu().numpy()[sample] if spec.reuse_tau > 0 else None
-    rt = reconcile_tc(spec, L64, rt, g_idx, g_reuse, max_frac=0.05)
-    ref = orc.layer_forward(spec, inp, xs, rt=rt, cache=None if cache_np is None else cache_np[sample])
-    assert_close(to_np(y)[sample], ref["y"], spec.dtype, spec.name + " sampled")
-    # properties that hold at any size
-    counts = rb["counts"].cpu().numpy()
-    n = int(rb["n_rows"][0])
-    rt_all = rb["row_token"][:n].cpu().numpy()
-    offs = rb["offsets"].cpu().numpy()
-    assert counts.sum() == n and offs[-1] == n
-    for e in range(spec.E_heavy):
-        seg = rt_all[offs[e]:offs[e + 1]]
-        assert np.all(np.diff(seg) >= 0)
-    return y
-
-
-def test_dit_moe_xl_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_dit_moe_xl_full_size():
     spec = WORKLOADS["dit_moe_xl"]
-    y1 = _sampled_tc_check(spec)
+    _, rt, y1, rb = _layer_case(spec)
+    g = routing_np(rb, spec)
+    assert g["n_rows"][0] == g["counts"].sum() == g["offsets"][-1] == spec.S * spec.k
     # determinism: a second call is bit-identical
-    y2 = _sampled_tc_check(spec)
+    inp = gen_layer_inputs(spec)
+    y2, _, _ = run_layer(spec, dev_tensor(inp.x, inp.bits["x"], "bf16"), upload_layer(inp))
     assert torch.equal(y1, y2)
 
 
-def test_dit_moe_xl_reuse_full_size_sampled():
-    _sampled_tc_check(WORKLOADS["dit_moe_xl_reuse"])
+@pytest.mark.timeout(600)
+def test_dit_moe_xl_reuse_full_size():
+    spec = WORKLOADS["dit_moe_xl_reuse"]
+    _, rt, _, rb = _layer_case(spec, with_cache=True)
+    n_reuse = int(rt["reuse"].sum())
+    say(f"  reused tokens: {n_reuse} of {spec.S}")
+    assert 0 < n_reuse < spec.S
+    assert int(rb["n_rows"][0]) == spec.k * (spec.S - n_reuse)
 
 
-def test_mmoe_first_layer_full_size_sampled():
-    _sampled_tc_check(WORKLOADS["mmoe"].replace(n_layers=1))
-
-
-def test_ec_dit_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_ec_dit_full_size():
     spec = WORKLOADS["ec_dit"]
-    inp = gen_layer_inputs(spec)
-    x = dev_tensor(inp.x, inp.bits["x"], "bf16")
-    y, logits, rb = run_layer(spec, x, upload_layer(inp))
-    L64 = orc.router_logits(inp.x, inp.w_router[0])
-    rt = _oracle_rt(spec, L64, rb)
-    C = rt["C"]
-    assert C == 512 and int(rb["n_rows"][0]) == 32 * 512
+    _, rt, _, rb = _layer_case(spec)
+    assert rt["C"] == 512 and int(rb["n_rows"][0]) == 32 * 512 and int(rb["capacity"][0]) == 512
     assert np.array_equal(rb["counts"].cpu().numpy(), np.full(32, 512))
-    sample = np.random.default_rng(9).choice(spec.S, size=40, replace=False)
-    ref = np.zeros((sample.size, spec.d))
-    for n, s in enumerate(sample):
-        for i in range(32):
-            hit = np.nonzero(rt["tokens"][i] == s)[0]
-            if hit.size:
-                ref[n] += rt["gates"][i][hit[0]] * orc.mlp(inp.x[s:s + 1], inp.w1[0][i], None, inp.w2[0][i], "gelu")[0]
-    assert_close(to_np(y)[sample], ref, "bf16", "ec_dit sampled")
+
+
+@pytest.mark.timeout(900)
+def test_mmoe_stack_full_size():
+    """All four MoE++ layers at 64 x 256 = 16384 tokens: routers above 1024 tokens take the 32-token
+    workgroups with the previous layer's logits added, and the GEMMs the benchmark's tile widths."""
+    _stack_case(WORKLOADS["mmoe"], end_to_end=False)

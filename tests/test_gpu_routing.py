@@ -6,7 +6,7 @@ import torch
 
 import mixture_experts_layer_gemm_amd as moe
 import oracle as orc
-from _gpu_helpers import reconcile_des, reconcile_ec, say
+from _gpu_helpers import reconcile_des, reconcile_des_seq, reconcile_ec, routing_np, say
 from synth import LayerSpec
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ def _route(spec, keys32, input_probs=False, multi=False):
     keys = torch.from_numpy(np.ascontiguousarray(keys32, np.float32)).cuda()
     moe.moe_route(desc, keys, rb.struct, ws)
     torch.cuda.synchronize()
-    return {k: v.cpu().numpy() for k, v in rb.tensors.items()}, rb
+    return routing_np(rb, spec), rb
 
 
 def _logits(rng, S, E, scale=0.7, tie_rows=0.2):
@@ -38,7 +38,7 @@ def _logits(rng, S, E, scale=0.7, tie_rows=0.2):
 
 def _check_permutation(spec, got, idx, reuse=None):
     E_r = spec.E_routed
-    valid = idx < spec.E_heavy
+    valid = (idx >= 0) & (idx < spec.E_heavy)       # -1: an empty DES-Seq slot
     if reuse is not None:
         valid &= ~reuse[:, None]
     counts, offsets, row_token, row_slot, token_rows = orc.counting_sort(idx, E_r, valid)
@@ -195,7 +195,7 @@ def test_des_route_dyadic_matches_bruteforce_core():
     got, _ = _route(spec, P32, input_probs=True)
     votes, core = orc.des_vote(P32, P32, K, M)
     assert np.array_equal(got["votes"].astype(np.float64), votes)
-    assert np.array_equal(got["core"], core)
+    assert np.array_equal(got["core"][:M], core)
 
 
 def test_des_route_on_logits_full_size():
@@ -205,9 +205,62 @@ def test_des_route_on_logits_full_size():
     got, _ = _route(spec, L)
     L64 = L.astype(np.float64)
     rt = orc.route(spec, L=L64)
-    rt = reconcile_des(spec, rt, got["core"], L64)
+    rt = reconcile_des(spec, rt, got["core"][: spec.m_core], L64)
     assert np.allclose(got["votes"], rt["votes"], atol=1e-6)
     assert np.array_equal(got["topk_idx"], rt["idx"])
+
+
+DES_SEQ_CASES = [
+    # N, E, k_seq, k
+    (32, 64, 1, 8),
+    (32, 64, 2, 8),
+    (32, 64, 4, 8),
+    (6, 10, 1, 4),      # small union: |core| may fall below k (empty slots)
+    (3, 40, 1, 8),      # |core| <= 3 < k
+    (100, 19, 3, 8),
+    (257, 128, 2, 16),
+    (60, 100, 2, 6),    # one-workgroup kernel with 2 experts per lane
+    (50, 150, 3, 8),    # and 4 per lane
+]
+
+
+@pytest.mark.parametrize("multi", [False, True])
+@pytest.mark.parametrize("case", DES_SEQ_CASES)
+def test_des_seq_route_bitexact_on_probs(case, multi):
+    """DES-Seq ("Dynamic Expert Sharing", 2.3, 4.3): core = union of the tokens' top-k_seq (listed
+    ascending, then -1), votes = selection counts, each token's top-min(k, |core|) inside the core,
+    the remaining slots empty; bit-exact on given fp32 probabilities with exact ties."""
+    N, E, kq, k = case
+    spec = _spec(S=N, E_heavy=E, mode="des_seq", k=k, vote_k=kq)
+    rng = np.random.default_rng(N * E + kq)
+    L = _logits(rng, N, E, scale=0.9, tie_rows=0.2).astype(np.float64)
+    P32 = orc.softmax(L).astype(np.float32)
+    say(f"des-seq route N={N} E={E} k_seq={kq} k={k} multi={multi}")
+    got, _ = _route(spec, P32, input_probs=True, multi=multi)
+    P = P32.astype(np.float64)
+    rt = orc.route(spec, P=P, input_probs=True)
+    n = rt["core"].size
+    assert np.array_equal(got["core"][:n], rt["core"]) and np.all(got["core"][n:] == -1)
+    assert np.array_equal(got["votes"], rt["votes"].astype(np.float32))
+    kp = rt["idx"].shape[1]
+    assert kp == min(k, n)
+    assert np.array_equal(got["topk_idx"][:, :kp], rt["idx"])
+    assert np.all(got["topk_idx"][:, kp:] == -1) and np.all(got["topk_w"][:, kp:] == 0)
+    assert np.allclose(got["topk_w"][:, :kp], rt["w"], rtol=k * 1.2e-7, atol=0)
+    idx = np.concatenate([rt["idx"], np.full((N, k - kp), -1)], axis=1)
+    _check_permutation(spec, got, idx)
+    assert set(np.flatnonzero(got["counts"])) <= set(rt["core"].tolist())
+
+
+def test_des_seq_route_on_logits_full_size():
+    spec = _spec(S=32, E_heavy=64, mode="des_seq", k=8, vote_k=2)
+    rng = np.random.default_rng(6)
+    L = (rng.standard_normal((32, 64)) * 0.91).astype(np.float32)
+    got, _ = _route(spec, L)
+    L64 = L.astype(np.float64)
+    rt = reconcile_des_seq(spec, orc.route(spec, L=L64), got["core"], L64)
+    kp = rt["idx"].shape[1]
+    assert np.array_equal(got["topk_idx"][:, :kp], rt["idx"])
 
 
 def test_route_is_deterministic():
