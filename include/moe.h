@@ -58,7 +58,9 @@ typedef enum {
                              e.g. the tiled expert GEMMs (used when experts get many rows) need
                              d and d_ff to be multiples of 64 */
   MOE_EWORKSPACE = -3,    /* ws_bytes < moe_workspace_bytes(desc) or ws not 256-byte aligned */
-  MOE_EHIP = -4           /* a HIP launch or runtime error (the call's work may be partly enqueued) */
+  MOE_EHIP = -4,          /* a HIP launch or runtime error (the call's work may be partly enqueued) */
+  MOE_ESCRATCH = -5       /* moe_layer_forward_noalloc: the call needs more scratch than its static
+                             buffer holds (moe_workspace_bytes(desc) > MOE_NOALLOC_SCRATCH_BYTES) */
 } moe_status;
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
@@ -190,6 +192,20 @@ moe_status moe_combine(const moe_desc *desc, const void *x, const moe_routing *r
 moe_status moe_layer_forward(const moe_desc *desc, const void *x, const moe_weights *weights,
                              const float *prev_logits, float *logits_out, moe_routing *routing, void *cache,
                              const void *residual, void *y, void *ws, size_t ws_bytes, void *stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory (code under stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same layer, the same kernels and results, with
+ * no workspace argument. Its scratch memory is a static device array of MOE_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) inside the library, one per GPU, held until the process ends; the call allocates nothing.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU (different streams, or
+ * threads) race and must be serialised by the caller. Runs on the current device, whose array
+ * address is looked up on the first call there. MOE_ESCRATCH when moe_workspace_bytes(desc) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES (e.g. beyond about 1300 tokens of the DiT-MoE-XL-shaped layer; decode
+ * blocks need about 2.5 MiB); otherwise the statuses of moe_layer_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_forward_noalloc(const moe_desc *desc, const void *x, const moe_weights *weights,
+                                     const float *prev_logits, float *logits_out, moe_routing *routing, void *cache,
+                                     const void *residual, void *y, void *stream);
 
 /* Attention-residual aggregation ("MMOE: Modernizing Diffusion Transformers with Efficient Expert
  * Design", 方法论: before a sub-layer a learned pseudo-query aggregates the completed block states,

@@ -11,7 +11,8 @@ import os
 from dataclasses import dataclass
 
 __all__ = [
-    "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP",
+    "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "MOE_ESCRATCH",
+    "MOE_NOALLOC_SCRATCH_BYTES", "moe_layer_forward_noalloc",
     "MOE_BF16", "MOE_F32", "MOE_ACT_GELU", "MOE_ACT_GELU_TANH", "MOE_ACT_SWIGLU",
     "MOE_TOKEN_CHOICE", "MOE_EXPERT_CHOICE", "MOE_DES_VOTE", "MOE_DES_SEQ",
     "MOE_F_INPUT_PROBS", "MOE_F_SYNC_DEBUG", "MOE_F_FORCE_TILED", "MOE_F_FORCE_STREAM", "MOE_F_ROUTE_MULTI",
@@ -21,7 +22,8 @@ __all__ = [
     "moe_layer_forward", "moe_strerror", "moe_profile_begin", "moe_profile_end", "moe_attnres_aggregate",
 ]
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4, -5
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 MOE_BF16, MOE_F32 = 0, 1
 MOE_ACT_GELU, MOE_ACT_GELU_TANH, MOE_ACT_SWIGLU = 0, 1, 2
 MOE_TOKEN_CHOICE, MOE_EXPERT_CHOICE, MOE_DES_VOTE, MOE_DES_SEQ = 0, 1, 2, 3
@@ -30,7 +32,7 @@ MOE_F_ROUTE_MULTI = 0x20
 
 # the layer's C ABI (include/moe.h) and the measurement hooks (include/moe_prof.h)
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_layer_forward", "moe_strerror", "moe_attnres_aggregate")
+           "moe_layer_forward", "moe_layer_forward_noalloc", "moe_strerror", "moe_attnres_aggregate")
 PROF_EXPORTS = ("moe_profile_begin", "moe_profile_end", "moe_profile_entry")
 
 _i32, _f32, _u32, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_uint32, ctypes.c_void_p
@@ -94,6 +96,9 @@ def lib() -> ctypes.CDLL:
         L.moe_layer_forward.restype = ctypes.c_int
         L.moe_layer_forward.argtypes = [P(MoeDesc), _vp, P(MoeWeights), _vp, _vp, P(MoeRouting), _vp, _vp, _vp,
                                         _vp, ctypes.c_size_t, _vp]
+        L.moe_layer_forward_noalloc.restype = ctypes.c_int
+        L.moe_layer_forward_noalloc.argtypes = [P(MoeDesc), _vp, P(MoeWeights), _vp, _vp, P(MoeRouting), _vp, _vp,
+                                                _vp, _vp]
         L.moe_attnres_aggregate.restype = ctypes.c_int
         L.moe_attnres_aggregate.argtypes = [_i32, _i32, _i32, _i32, P(_vp), _vp, _f32, _vp, _vp]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -184,6 +189,15 @@ def moe_layer_forward(desc, x, weights: MoeWeights, prev_logits, logits_out, rou
                                  _ptr(logits_out), rp, _ptr(cache), _ptr(residual), _ptr(y), _ptr(ws), nb,
                                  _stream(stream))
     return _check(st, "moe_layer_forward", raise_on_error)
+
+
+def moe_layer_forward_noalloc(desc, x, weights: MoeWeights, prev_logits, logits_out, routing, cache, residual, y,
+                              stream=None, raise_on_error=True) -> int:
+    """moe_layer_forward with the library's static scratch array in place of a workspace."""
+    rp = ctypes.byref(routing) if routing is not None else None
+    st = lib().moe_layer_forward_noalloc(ctypes.byref(desc), _ptr(x), ctypes.byref(weights), _ptr(prev_logits),
+                                         _ptr(logits_out), rp, _ptr(cache), _ptr(residual), _ptr(y), _stream(stream))
+    return _check(st, "moe_layer_forward_noalloc", raise_on_error)
 
 
 def moe_profile_begin() -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libmoe.so")
 OBJ = os.path.join(ROOT, "_build", "obj")
-SOURCES = ["api.cpp", "route.hip", "ec.hip", "combine.hip", "gemm.hip", "stream.hip", "attnres.hip"]
+SOURCES = ["api.cpp", "route.hip", "ec.hip", "combine.hip", "gemm.hip", "stream.hip", "attnres.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -645,6 +645,7 @@ const char* moe_strerror(int status) {
     case MOE_EUNSUPPORTED: return "unsupported configuration";
     case MOE_EWORKSPACE: return "workspace too small or misaligned";
     case MOE_EHIP: return "HIP runtime or launch error";
+    case MOE_ESCRATCH: return "the call needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown status";
   }
 }

@@ -27,10 +27,10 @@ def _declared(header="moe.h"):
     return set(re.findall(r"^\s*(?:const\s+char\s*\*\s*|size_t\s+|moe_status\s+|int\s+)(moe_\w+)\s*\(", src, flags=re.M))
 
 
-# The layer's boundary: the five calls of the hot path, the two helpers, and the MMOE block-level
-# aggregation next to the layer.
+# The layer's boundary: the five calls of the hot path, the two helpers, the variant of
+# moe_layer_forward that allocates nothing, and the MMOE block-level aggregation next to the layer.
 LAYER_ABI = {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
-             "moe_workspace_bytes", "moe_strerror", "moe_attnres_aggregate"}
+             "moe_workspace_bytes", "moe_strerror", "moe_layer_forward_noalloc", "moe_attnres_aggregate"}
 
 
 def _exported():
@@ -50,7 +50,7 @@ def test_exports_exactly_the_declared_entry_points():
 
 def test_strerror():
     assert moe.moe_strerror(0) == "ok"
-    for s in (-1, -2, -3, -4):
+    for s in (-1, -2, -3, -4, -5):
         assert moe.moe_strerror(s) != "unknown status"
     assert moe.moe_strerror(-99) == "unknown status"
 
@@ -179,3 +179,17 @@ def test_attnres_argument_checks():
     assert call(moe.MOE_BF16, 4, 64, [a] * 65, q, 1e-6, o, stream=0, raise_on_error=False) == moe.MOE_EUNSUPPORTED
     with pytest.raises(moe.MoeError):
         call(moe.MOE_BF16, 4, 64, [], q, 1e-6, o, stream=0)
+
+
+def test_noalloc_rejects_before_any_launch():
+    """The no-allocation entry point validates on the host: a description whose scratch exceeds the
+    static buffer gives MOE_ESCRATCH, an invalid or unsupported one the status moe_layer_forward gives."""
+    w = moe.MoeWeights(*([FAKE] * 8))
+    big = moe.desc_from_spec(WORKLOADS["dit_moe_xl"])                       # about 397 MiB of scratch
+    assert moe.moe_workspace_bytes(big) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert moe.moe_layer_forward_noalloc(big, FAKE, w, None, None, None, None, None, FAKE, stream=0,
+                                         raise_on_error=False) == moe.MOE_ESCRATCH
+    assert moe.moe_layer_forward_noalloc(_desc(k=0), FAKE, w, None, None, None, None, None, FAKE, stream=0,
+                                         raise_on_error=False) == moe.MOE_EINVAL
+    assert moe.moe_layer_forward_noalloc(_desc(d=1160), FAKE, w, None, None, None, None, None, FAKE, stream=0,
+                                         raise_on_error=False) == moe.MOE_EUNSUPPORTED
