@@ -8,8 +8,9 @@
 // experts are extra problems in the same launch (all S rows; their down projections are one GEMM
 // over the K-concatenation of their hidden activations).
 //
-// Design (one workgroup = 4 waves, one per SIMD, = one 256 x BN tile, BN in {128, 192, 256}; each wave
-// owns 128 token rows x BN/2 weight rows, the 2 x 2 split with the fewest LDS reads per MFMA):
+// Design (one workgroup = one 256 x BN tile, BN in {128, 192, 256}, of 4 waves, one per SIMD, each
+// owning 128 token rows x BN/2 weight rows, the 2 x 2 split with the fewest LDS reads per MFMA; the
+// GELU up projections use 8 waves, two per SIMD, each owning 128 x BN/4):
 //   * K advances in blocks of two MFMA K steps: 128 bytes of every tile row, one whole cache line,
 //     so every 16-byte-per-lane load instruction reads 8 full lines (reading 64-byte halves made
 //     twice the L2 requests for the same bytes, and the L2 request rate was the limit).
@@ -46,9 +47,16 @@ constexpr int kStepB = 64;          // bytes of one tile row per MFMA K step
 constexpr int kUnits = 5;           // LDS ring of 32 KB units; the A and B units of the K blocks alternate
 constexpr int kUnitB = 32768;
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
-constexpr int kWaves = 4;           // 2 x 2 wave grid, one wave per SIMD
-constexpr int kThreads = 64 * kWaves;
 constexpr int kGM = 4;              // m-tiles per sweep group
+
+// Compile-time loop over 0..N-1 (every index a constant, so register arrays stay in registers).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
 
 struct GemmLaunch {
   GemmProblem p0, p1;
@@ -148,17 +156,23 @@ struct step_sched {
   }
 };
 
-template <typename T, int KIND, int ACT, int BN>
-__global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
+// WV waves per workgroup: 4 (one per SIMD, each wave 128 x BN/2 outputs) or 8 (two per SIMD, each
+// 128 x BN/4: a wave that stalls on a load, an LDS read or the barrier leaves the matrix core to the
+// other wave of its SIMD).
+template <typename T, int KIND, int ACT, int BN, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void k_grouped_gemm(GemmLaunch args) {
   constexpr int EPC = Elem<T>::kPer16B;        // elements per 16-byte chunk
   constexpr int BK = kStepB / sizeof(T);       // K elements per MFMA step
   constexpr int BU = 2 * BK;                   // K elements per unit (one K block)
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
-  constexpr int NI = BN / 32;                  // 16-row n-subtiles per wave (wave covers BN/2 B rows)
+  constexpr int WN = WV / 2;                   // wave grid: 2 rows of WN waves
+  constexpr int NI = BN / (16 * WN);           // 16-row n-subtiles per wave (wave covers BN/WN B rows)
   constexpr int MJ = 8;                        // 16-row m-subtiles per wave (wave covers 128 rows)
   constexpr int NF = MJ + NI;                  // fragments per K step
-  constexpr int A_LD = kBM / (kRowsPerLoad * kWaves);   // wave load instructions per A unit
-  constexpr int B_LD = BN / (kRowsPerLoad * kWaves);    // per B unit
+  constexpr int A_LD = kBM / (kRowsPerLoad * WV);   // wave load instructions per A unit
+  constexpr int B_LD = BN / (kRowsPerLoad * WV);    // per B unit
+  static_assert(BN % (16 * WN) == 0 && (!SWIGLU || NI % 2 == 0), "whole n-subtiles per wave (gate and up halves)");
+  static_assert(A_LD * kRowsPerLoad * WV == kBM && B_LD * kRowsPerLoad * WV == BN, "whole loads per unit");
   static_assert(kBM * kRowB <= kUnitB && BN * kRowB <= kUnitB, "a unit holds one K block of A or of B");
   // One array per ring unit: with the K loop unrolled every LDS access names its unit at compile
   // time. Five 32 KB units are all of LDS; nothing else in the kernel uses LDS.
@@ -196,10 +210,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   // ---- per-lane source offsets. Load instruction i of wave w fills the 128-byte rows
-  // i*8*kWaves + 8w .. +8 of a unit; lane l writes row r = i*8*kWaves + 8w + l/8 at slot l%8, i.e. the
+  // i*8*WV + 8w .. +8 of a unit; lane l writes row r = i*8*WV + 8w + l/8 at slot l%8, i.e. the
   // chunk (l%8) ^ ((r >> 1) & 7) of that row. Eight lanes read one whole cache line.
   const T* __restrict__ Ab = (const T*)P.A;
   const T* __restrict__ Bb = (const T*)P.B + (size_t)g * P.b_gstride;
@@ -209,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   bool b_gate[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 3);
+    const int r = i * kRowsPerLoad * WV + wave * kRowsPerLoad + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int orow = row0 + min(r, rows - 1);
     const int arow = P.a_rows ? P.a_rows[orow] : orow;
@@ -217,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
   }
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int r = i * kRowsPerLoad * kWaves + wave * kRowsPerLoad + (lane >> 3);
+    const int r = i * kRowsPerLoad * WV + wave * kRowsPerLoad + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     const bool gate = SWIGLU && r >= BN / 2;   // the same for the whole wave
     b_gate[i] = gate;
@@ -264,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     }
     return d;
   };
-  constexpr uint32_t kLoadStride = kRowsPerLoad * kWaves * kRowB;   // LDS bytes between a wave's loads
+  constexpr uint32_t kLoadStride = kRowsPerLoad * WV * kRowB;   // LDS bytes between a wave's loads
   auto dma_a = [&](const Dma& d, auto Qc) {
     constexpr int q = decltype(Qc)::value;
     gload_lds16(d.p, a_off[q], d.lds + q * kLoadStride);
@@ -273,41 +287,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     constexpr int i = decltype(Qc)::value;
     gload_lds16(b_gate[i] ? d.p3 : d.p, b_off[i], d.lds + i * kLoadStride);
   };
-  auto issue_a = [&](const Dma& d) {
-    dma_a(d, std::integral_constant<int, 0>{});
-    dma_a(d, std::integral_constant<int, 1>{});
-    dma_a(d, std::integral_constant<int, 2>{});
-    dma_a(d, std::integral_constant<int, 3>{});
-    dma_a(d, std::integral_constant<int, 4>{});
-    dma_a(d, std::integral_constant<int, 5>{});
-    dma_a(d, std::integral_constant<int, 6>{});
-    dma_a(d, std::integral_constant<int, 7>{});
-    static_assert(A_LD == 8, "eight loads per A unit");
-  };
+  auto issue_a = [&](const Dma& d) { static_for<A_LD>([&](auto Qc) { dma_a(d, Qc); }); };
   // The ring alternates the units of two operands: L, whose loads start three MFMA steps before
   // it is first read, and S, two steps (below). The up projections give the weights the longer
   // lead, the down projections the tokens (measured on the dense SwiGLU up and long-K down shapes).
   constexpr bool B_LONG = KIND == GEMM_UP;
   constexpr int L_LD = B_LONG ? B_LD : A_LD, S_LD = B_LONG ? A_LD : B_LD;
-  auto issue_b = [&](const Dma& d) {
-    dma_b(d, std::integral_constant<int, 0>{});
-    dma_b(d, std::integral_constant<int, 1>{});
-    dma_b(d, std::integral_constant<int, 2>{});
-    dma_b(d, std::integral_constant<int, 3>{});
-    if constexpr (B_LD > 4) dma_b(d, std::integral_constant<int, 4>{});
-    if constexpr (B_LD > 5) dma_b(d, std::integral_constant<int, 5>{});
-    if constexpr (B_LD > 6) dma_b(d, std::integral_constant<int, 6>{});
-    if constexpr (B_LD > 7) dma_b(d, std::integral_constant<int, 7>{});
-    static_assert(B_LD >= 4 && B_LD <= 8, "four to eight loads per B unit");
-  };
+  auto issue_b = [&](const Dma& d) { static_for<B_LD>([&](auto Qc) { dma_b(d, Qc); }); };
 
   // B-tile row of n-subtile i for this wave.
   auto brow_of = [&](int i) -> int {
     if (SWIGLU) {
       constexpr int H = NI / 2;
-      return i < H ? wn * (BN / 4) + i * 16 : BN / 2 + wn * (BN / 4) + (i - H) * 16;
+      return i < H ? wn * (BN / (2 * WN)) + i * 16 : BN / 2 + wn * (BN / (2 * WN)) + (i - H) * 16;
     }
-    return wn * (BN / 2) + i * 16;
+    return wn * (BN / WN) + i * 16;
   };
 
   floatx4_t acc[NI][MJ];
@@ -435,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
 
   // ---- epilogue: lane holds rows (m) = wm*128 + j*16 + fr, columns 4*fg + t of n-subtile i
   const int64_t col_base = (int64_t)g * P.c_gcol;
-  if constexpr (SWIGLU && BN == 256 && sizeof(T) == 2) {
+  if constexpr (SWIGLU && BN == 256 && sizeof(T) == 2 && WV == 4) {
     // SwiGLU with 256-wide tiles: each wave's 128 x 64 bf16 outputs (128 bytes per row) go through
     // LDS, so that every store instruction writes 8 whole 128-byte lines instead of 16 rows x 32
     // bytes. 16-byte chunk c of staged row r sits at slot c ^ (r & 7). The ring is free once every
@@ -468,7 +462,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
     }
     return;
   }
-  if constexpr (KIND == GEMM_DOWN && BN == 256) {
+  if constexpr (KIND == GEMM_UP && !SWIGLU && BN == 256 && WV == 8 && sizeof(T) == 2) {
+    // GELU with 256-wide tiles and 8 waves: each wave's 128 x 64 bf16 outputs (128 bytes per row, one
+    // cache line) go through its own 16 KB of the freed ring, so that every store instruction writes 8
+    // whole lines instead of 16 rows x 32 bytes. 16-byte chunk c of staged row r sits at slot c ^ (r & 7).
+    ring_barrier();
+    uint8_t* stage = (wave < 2 ? smem0 : wave < 4 ? smem1 : wave < 6 ? smem2 : smem3) + (wave & 1) * (128 * 128);
+#pragma unroll
+    for (int j = 0; j < MJ; ++j)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float h[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) h[t] = ACT == ACT_GELU_TANH ? gelu_tanh(acc[i][j][t]) : gelu_erf(acc[i][j][t]);
+        uint2 v;
+        v.x = pack2_bf16(h[0], h[1]);
+        v.y = pack2_bf16(h[2], h[3]);
+        const int r = j * 16 + fr, c = 2 * i + (fg >> 1);
+        *reinterpret_cast<uint2*>(stage + r * 128 + ((c ^ (r & 7)) << 4) + (fg & 1) * 8) = v;
+      }
+    asm volatile("" ::: "memory");   // the wave's LDS accesses run in order; keep the compiler's too
+    const int c = lane & 7;
+    const int n = nt * BN + wn * (BN / WN) + c * 8;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = q * 8 + (lane >> 3);
+      const uint4 v = *reinterpret_cast<const uint4*>(stage + r * 128 + ((c ^ (r & 7)) << 4));
+      const int ml = wm * 128 + r;
+      if (ml >= rows || n >= P.N) continue;
+      *reinterpret_cast<uint4*>((T*)P.C + (row0 + ml) * P.ldc + col_base + n) = v;
+    }
+    return;
+  }
+  if constexpr (KIND == GEMM_DOWN && BN == 256 && WV == 4) {
     // fp32 outputs with 256-wide tiles: each wave's 128 x 128 outputs go through its own 32 KB unit
     // in two halves of 64 rows (512 bytes per row), 16-byte chunk c of row r at slot c ^ (r & 15);
     // each store instruction then writes 2 rows x 512 bytes (8 whole lines) instead of 16 rows x
@@ -519,7 +545,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
           else if (ACT == ACT_GELU_TANH) h[t] = gelu_tanh(u);
           else h[t] = gelu_erf(u);
         }
-        const int n = SWIGLU ? nt * (BN / 2) + wn * (BN / 4) + i * 16 + 4 * fg : nt * BN + wn * (BN / 2) + i * 16 + 4 * fg;
+        const int n = SWIGLU ? nt * (BN / 2) + wn * (BN / (2 * WN)) + i * 16 + 4 * fg
+                             : nt * BN + wn * (BN / WN) + i * 16 + 4 * fg;
         if (n >= P.N) continue;
         if (sizeof(T) == 2) {
           uint2 v;
@@ -534,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped_gemm(GemmLaunch args) {
       float* crow = (float*)P.C + orow * P.ldc + col_base;
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int n = nt * BN + wn * (BN / 2) + i * 16 + 4 * fg;
+        const int n = nt * BN + wn * (BN / WN) + i * 16 + 4 * fg;
         if (n >= P.N) continue;
         *reinterpret_cast<float4*>(crow + n) = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
@@ -603,17 +630,23 @@ bool grouped_gemm_supported(int dtype, int kind, int act, int N, int K) {
   return N > 0 && N % 64 == 0 && K > 0 && K % bu == 0;
 }
 
-template <typename T, int KIND, int ACT, int BN>
+template <typename T, int KIND, int ACT, int BN, int WV>
 static void launch_t(const GemmLaunch& la, int grid, hipStream_t st) {
-  auto kfn = k_grouped_gemm<T, KIND, ACT, BN>;
-  MOE_LAUNCH(KIND == GEMM_UP ? "gemm_up" : "gemm_down", kfn, grid, kThreads, 0, st, la);
+  auto kfn = k_grouped_gemm<T, KIND, ACT, BN, WV>;
+  MOE_LAUNCH(KIND == GEMM_UP ? "gemm_up" : "gemm_down", kfn, grid, 64 * WV, 0, st, la);
 }
 
+// Waves per workgroup. Eight (two per SIMD) for the bf16 GELU up projections with 256-wide tiles:
+// their long activation epilogue and the main loop's issue stalls then share each SIMD with a
+// second wave (mmoe: 537 -> 516 us per layer on one box). Four everywhere else: with eight, the
+// waves read 1.5x the LDS fragments per MFMA and the down projections lose the LDS-staged store
+// (mmoe down 431 -> 475 us, dit_moe_xl down 313 -> 354 us); the SwiGLU up projection was unchanged.
 template <typename T, int KIND, int ACT>
 static void launch_bn(const GemmLaunch& la, int bn, int grid, hipStream_t st) {
-  if (bn == 256) launch_t<T, KIND, ACT, 256>(la, grid, st);
-  else if (bn == 192) launch_t<T, KIND, ACT, 192>(la, grid, st);
-  else launch_t<T, KIND, ACT, 128>(la, grid, st);
+  constexpr bool W8 = sizeof(T) == 2 && KIND == GEMM_UP && ACT != ACT_SWIGLU;
+  if (bn == 256) launch_t<T, KIND, ACT, 256, W8 ? 8 : 4>(la, grid, st);
+  else if (bn == 192) launch_t<T, KIND, ACT, 192, 4>(la, grid, st);
+  else launch_t<T, KIND, ACT, 128, 4>(la, grid, st);
 }
 
 template <typename T>

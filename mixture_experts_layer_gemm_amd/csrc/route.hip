@@ -267,11 +267,16 @@ static void route_topk_t(const RouteArgs& a, hipStream_t st) {
   MOE_LAUNCH("route_topk", kfn, (a.S + 256 / LPT - 1) / (256 / LPT), 256, 0, st, a);
 }
 
+// Lanes per token (LPT) and experts per lane (V) for E_r routed experts, the same in every routing
+// kernel (the softmax sums a token's experts per lane, then over its lanes, so the mapping fixes the
+// rounding): up to 32 experts, 8 lanes of up to 4 experts, so a wave routes 8 tokens at once with
+// 3-level shuffle reductions (mmoe, 19 experts: 6.9 -> 4.2 us); beyond, a whole wave per token,
+// whose top-k is a radix select over ballots (cross-lane shuffles go through the LDS crossbar, and
+// k rounds of 4- or 5-level shuffle reductions cost more than the ballots at 64 experts).
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st) {
   const int E = a.E_r;
   if (E <= 8) route_topk_t<8, 1>(a, st);
-  else if (E <= 16) route_topk_t<16, 1>(a, st);
-  else if (E <= 32) route_topk_t<32, 1>(a, st);
+  else if (E <= 32) route_topk_t<8, 4>(a, st);
   else if (E <= 64) route_topk_t<64, 1>(a, st);
   else if (E <= 128) route_topk_t<64, 2>(a, st);
   else route_topk_t<64, 4>(a, st);
@@ -404,10 +409,9 @@ static void route_des_t(const RouteArgs& a, float* ws_filt, hipStream_t st) {
 }
 
 hipError_t launch_route_des(const RouteArgs& a, float* ws_filt, hipStream_t st) {
-  const int E = a.E_r;
+  const int E = a.E_r;   // the lane mapping of launch_route_topk
   if (E <= 8) route_des_t<8, 1>(a, ws_filt, st);
-  else if (E <= 16) route_des_t<16, 1>(a, ws_filt, st);
-  else if (E <= 32) route_des_t<32, 1>(a, ws_filt, st);
+  else if (E <= 32) route_des_t<8, 4>(a, ws_filt, st);
   else if (E <= 64) route_des_t<64, 1>(a, ws_filt, st);
   else if (E <= 128) route_des_t<64, 2>(a, ws_filt, st);
   else route_des_t<64, 4>(a, ws_filt, st);
@@ -929,10 +933,9 @@ static void route_small_t(const RouteArgs& a, const PermuteArgs& q, bool des, hi
 hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st) {
   const int kk = des ? (a.seq ? a.k : std::min(a.k, a.m_core)) : a.k;
   if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > 256 || q.k != kk) return hipErrorInvalidValue;
-  const int E = a.E_r;
+  const int E = a.E_r;   // the lane mapping of launch_route_topk
   if (E <= 8) route_small_t<8, 1>(a, q, des, st);
-  else if (E <= 16) route_small_t<16, 1>(a, q, des, st);
-  else if (E <= 32) route_small_t<32, 1>(a, q, des, st);
+  else if (E <= 32) route_small_t<8, 4>(a, q, des, st);
   else if (E <= 64) route_small_t<64, 1>(a, q, des, st);
   else if (E <= 128) route_small_t<64, 2>(a, q, des, st);
   else route_small_t<64, 4>(a, q, des, st);
