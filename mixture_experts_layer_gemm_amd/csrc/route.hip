@@ -62,7 +62,8 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
     for (int p = 0; p < TT; ++p) acc[p][q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
   const int nsteps = d / STEP;
-#pragma unroll 2
+  // a wave takes about four K steps: unrolled, all of their loads are in flight together
+#pragma unroll 4
   for (int t = wave; t < nsteps; t += W) {
     const size_t kk = (size_t)t * STEP;
     uint4 xv[TT];

@@ -247,14 +247,39 @@ def test_mmoe_stack_reduced():
     _stack_case(WORKLOADS["mmoe"].replace(S=600))
 
 
-def test_four_call_path_matches_layer_forward():
-    """moe_route + moe_dispatch + moe_expert_ffn + moe_combine == moe_layer_forward (bitwise)."""
-    spec = WORKLOADS["dit_moe_xl"].replace(S=513)
+FOUR_CALL_CASES = {
+    # grouped GEMMs, then the combine kernel
+    "dit_moe_xl": (WORKLOADS["dit_moe_xl"].replace(S=513), 0, False, False),
+    # weight streaming: moe_layer_forward combines inside the streaming down projection, the
+    # four-call path with the combine kernel
+    "des_vote_b025": (WORKLOADS["des_vote_b025"], 0, False, False),
+    "des_seq_k1": (WORKLOADS["des_seq"].replace(vote_k=1), 0, False, False),
+    # shared and zero-computation experts, residual: the shared GEMMs run before the streamed experts
+    "mmoe_stream": (WORKLOADS["mmoe"].replace(S=64, d=256, f=512, n_layers=1), moe.MOE_F_FORCE_STREAM, False, True),
+    # cached routed parts of low-score tokens (written by the fused combine for fresh tokens)
+    "reuse_stream": (WORKLOADS["dit_moe_xl_reuse"].replace(S=96, d=384, f=256, reuse_tau=0.2), moe.MOE_F_FORCE_STREAM,
+                     True, True),
+}
+
+
+@pytest.mark.parametrize("name", list(FOUR_CALL_CASES))
+def test_four_call_path_matches_layer_forward(name):
+    """moe_route + moe_dispatch + moe_expert_ffn + moe_combine == moe_layer_forward (bitwise), also
+    where the layer forward fuses the combine into the streaming down projection."""
+    spec, flags, with_cache, residual = FOUR_CALL_CASES[name]
+    say(f"four-call {name}: S={spec.S} d={spec.d} f={spec.f} flags={flags}")
     inp = gen_layer_inputs(spec, seed=4)
     x = dev_tensor(inp.x, inp.bits["x"], "bf16")
     wt = upload_layer(inp)
-    y_ref, logits, _ = run_layer(spec, x, wt)
-    desc = moe.desc_from_spec(spec)
+    cache0 = None
+    if with_cache:
+        rng = np.random.default_rng(9)
+        cv, cb = gen_tensor(rng, (spec.S, spec.d), 0.5, spec.dtype)
+        cache0 = dev_tensor(cv, cb, spec.dtype)
+    res = x if residual else None
+    c_a = cache0.clone() if with_cache else None
+    y_ref, logits, _ = run_layer(spec, x, wt, flags=flags, cache=c_a, residual=res)
+    desc = moe.desc_from_spec(spec, flags)
     rb = moe.alloc_routing(desc)
     ws = moe.workspace(desc)
     moe.moe_route(desc, logits, rb.struct, ws)
@@ -265,12 +290,18 @@ def test_four_call_path_matches_layer_forward():
     w = moe.weights_struct(wt)
     moe.moe_expert_ffn(desc, x, xp, rb.struct, w, yp, ys, ws)
     y = torch.empty_like(x)
-    moe.moe_combine(desc, x, rb.struct, yp, ys, None, None, None, y)
+    c_b = cache0.clone() if with_cache else None
+    moe.moe_combine(desc, x, rb.struct, yp, ys, wt.get("const_vec"), c_b, res, y)
     torch.cuda.synchronize()
     n = int(rb["n_rows"][0])
     tok = rb["row_token"][:n].long()
     assert torch.equal(xp[:n], x[tok])
     assert torch.equal(y, y_ref)
+    if with_cache:
+        reused = rb["reuse"].bool()
+        assert 0 < int(reused.sum()) < spec.S
+        assert torch.equal(c_a, c_b)
+        assert torch.equal(c_a[reused], cache0[reused])
 
 
 # ------------------------------------------------------------------------------------------------
