@@ -136,6 +136,15 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 // ---------------------------------------------------------------------------------------------
 // Direct global -> LDS loads and their waits (grouped GEMM and weight streaming).
+// Compile-time loop over 0..N-1 (every index a constant, so register arrays stay in registers).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 // 16 bytes per lane from global memory (wave-uniform base + per-lane byte offset) straight into

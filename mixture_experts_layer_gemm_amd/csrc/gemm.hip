@@ -49,15 +49,6 @@ constexpr int kUnitB = 32768;
 constexpr int kRowsPerLoad = 1024 / kRowB;   // rows one wave-wide 16-byte-per-lane load fills
 constexpr int kGM = 4;              // m-tiles per sweep group
 
-// Compile-time loop over 0..N-1 (every index a constant, so register arrays stay in registers).
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 struct GemmLaunch {
   GemmProblem p0, p1;
   int32_t tiles_n0, tiles_n1;

@@ -22,9 +22,8 @@
 
 namespace moe {
 
-// The slot-th expert (ascending id) with at least one row, or -1.
-__device__ __forceinline__ int locate_active(const GemmProblem& P, int slot) {
-  __shared__ int s_e;
+// The slot-th expert (ascending id) with at least one row, or -1. s_e: one int of LDS to pass it on.
+__device__ __forceinline__ int locate_active(const GemmProblem& P, int slot, int* s_e) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int carry = 0, found = -1;
@@ -37,10 +36,10 @@ __device__ __forceinline__ int locate_active(const GemmProblem& P, int slot) {
       if (hit) found = g0 + __ffsll((unsigned long long)hit) - 1;
       carry += __popcll(m);
     }
-    if (lane == 0) s_e = found;
+    if (lane == 0) *s_e = found;
   }
   __syncthreads();
-  return s_e;
+  return *s_e;
 }
 
 // G (16-column groups) x SL (K slices) waves per workgroup
@@ -52,8 +51,9 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
   constexpr int NACC = SWIGLU ? 4 : 2;   // floatx4 accumulators per lane: 2 token groups (x gate)
   __shared__ floatx4_t s_red[SL - 1][G][NACC][64];
+  __shared__ int s_e;
   const GemmProblem& P = la_p;
-  const int e = locate_active(P, blockIdx.y);
+  const int e = locate_active(P, blockIdx.y, &s_e);
   if (e < 0) return;
   const int beg = P.offsets[e];
   const int cnt = P.offsets[e + 1] - beg;
@@ -159,13 +159,13 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
 // of one active expert; wave w takes the K stages w, w + 4, w + 8, ... (one MFMA K step, 64 bytes
 // of every row, per stage), so the four waves read neighbouring 64-byte pieces of each row at the
 // same time. Each wave streams its stages, weight rows and the 16 * GRP token rows of the pass
-// alike, through a private ring of kRingSlots LDS slots with direct global->LDS loads,
-// kRingSlots - 1 stages in flight while one is multiplied: no barrier inside the loop and no
+// alike, through a private ring of D LDS slots (3 or 4) with direct global->LDS loads,
+// D - 1 stages in flight while one is multiplied: no barrier inside the loop and no
 // register staging. The four partial sums are added in LDS in wave order at the end. GRP (2 or 4
 // groups of 16 token rows per pass) comes from the host: an expert with more rows than a pass
 // serves streams its weights once per pass.
 constexpr int kRingRows = 64;    // weight rows per workgroup (x 2 with SwiGLU)
-constexpr int kRingSlots = 3;    // stages per wave ring
+constexpr int kRingSlots = 3;    // fewest stages per wave ring
 constexpr int kRingRowB = 64;    // bytes of one row per stage
 constexpr int kRingStageK = 4 * kRingRowB / 2;   // K elements per round of the 4 waves (bf16)
 
@@ -181,7 +181,8 @@ __device__ __forceinline__ void gload_lds16_va(const void* addr, uint32_t lds) {
                : "memory", "m0");
 }
 
-template <int KIND, int ACT, int GRP>
+// D: ring slots per wave (D - 1 stages in flight)
+template <int KIND, int ACT, int GRP, int D>
 __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   using T = bf16_t;
   constexpr int EPC = Elem<T>::kPer16B;
@@ -194,12 +195,15 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   constexpr int PER = LPS + GRP;                                // loads per stage
   constexpr int NT = kRingRows / 16;                            // 16-column subtiles (= waves)
   constexpr int NB = SWIGLU ? 2 * NT : NT;                      // weight fragments per stage
-  constexpr int D = kRingSlots;
   static_assert(NT == 4, "one subtile per wave in the epilogue");
+  static_assert(D >= 3 && (D - 2) * PER < 64, "stages in flight within the wait counter");
   static_assert(4 * GRP * NB * 64 * 16 <= 4 * D * SLOT, "reduction fits in the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][D][SLOT];
   const GemmProblem& P = la_p;
-  const int e = __builtin_amdgcn_readfirstlane(locate_active(P, blockIdx.y));
+  // the expert comes through the ring's first word (the ring may fill all of LDS); every thread
+  // has read it before any load into the ring is issued
+  const int e = __builtin_amdgcn_readfirstlane(locate_active(P, blockIdx.y, reinterpret_cast<int*>(&ring[0][0][0])));
+  __syncthreads();
   if (e < 0) return;
   const int beg = P.offsets[e];
   const int cnt = P.offsets[e + 1] - beg;
@@ -259,23 +263,24 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[g][i] = mfma16(bf[i], xv[g], acc[g][i], T());
     };
-    static_assert(D == 3, "the tail below drains a 3-slot ring");
-    issue(0);
-    issue(1);
-    // stage s: wait for it (stage s + 1 stays in flight) and for the LDS reads of stage s - 1,
-    // refill that slot with stage s + 2, multiply
-    for (int s = 0; s + 2 < ns; ++s) {
-      __builtin_amdgcn_s_waitcnt((PER & 15) | (((PER >> 4) & 3) << 14) | (7 << 4));   // + lgkmcnt(0)
+    // ns >= D - 1 (stream_ring_supported and the launcher's choice of D)
+    static_for<D - 1>([&](auto Sc) { issue(decltype(Sc)::value); });
+    // stage s: wait for it (stages s + 1 .. s + D - 2 stay in flight) and for the LDS reads of
+    // stage s - 1, refill that slot with stage s + D - 1, multiply
+    constexpr int INF = (D - 2) * PER;
+    for (int s = 0; s + D - 1 < ns; ++s) {
+      __builtin_amdgcn_s_waitcnt((INF & 15) | (((INF >> 4) & 3) << 14) | (7 << 4));   // + lgkmcnt(0)
       asm volatile("" ::: "memory");
-      issue(s + 2);
+      issue(s + D - 1);
       compute(s);
     }
-    wait_vmem<PER>();
-    asm volatile("" ::: "memory");
-    compute(ns - 2);
-    wait_vmem<0>();
-    asm volatile("" ::: "memory");
-    compute(ns - 1);
+    // drain: the last D - 1 stages, each once the stages after it are the only ones in flight
+    static_for<D - 1>([&](auto Jc) {
+      constexpr int left = D - 2 - decltype(Jc)::value;   // stages still in flight after this one
+      wait_vmem<left * PER>();
+      asm volatile("" ::: "memory");
+      compute(ns - 1 - left);
+    });
     // add the four waves' partial sums in wave order; wave w finishes subtile w
     __syncthreads();
     floatx4_t* red = reinterpret_cast<floatx4_t*>(&ring[0][0][0]);   // [wave][g][NB][64]
@@ -324,16 +329,28 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   }
 }
 
+// Ring depth: the SwiGLU up projection with 32-row passes (10 KB stages, a whole compute unit per
+// workgroup) takes a fourth slot, which fills the 160 KB of LDS: three stages in flight per wave
+// instead of two. The other shapes keep three slots, which lets two workgroups share a compute unit
+// (GELU and down projections: 6 KB stages).
 template <int KIND, int ACT>
 static void ring_t(const GemmProblem& la, int max_active, int pass_rows, hipStream_t st) {
   const dim3 grid(la.N / kRingRows, max_active);
+  const char* name = KIND == GEMM_UP ? "stream_up" : "stream_down";
   if (pass_rows > 32) {
-    auto kfn = k_stream_ring<KIND, ACT, 4>;
-    MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
-  } else {
-    auto kfn = k_stream_ring<KIND, ACT, 2>;
-    MOE_LAUNCH(KIND == GEMM_UP ? "stream_up" : "stream_down", kfn, grid, 256, 0, st, la);
+    auto kfn = k_stream_ring<KIND, ACT, 4, 3>;
+    MOE_LAUNCH(name, kfn, grid, 256, 0, st, la);
+    return;
   }
+  if constexpr (KIND == GEMM_UP && ACT == ACT_SWIGLU) {
+    if (la.K / kRingStageK >= 3) {
+      auto kfn = k_stream_ring<KIND, ACT, 2, 4>;
+      MOE_LAUNCH(name, kfn, grid, 256, 0, st, la);
+      return;
+    }
+  }
+  auto kfn = k_stream_ring<KIND, ACT, 2, 3>;
+  MOE_LAUNCH(name, kfn, grid, 256, 0, st, la);
 }
 
 bool stream_gemm_supported(int dtype, int kind, int act, int N, int K) {
