@@ -65,6 +65,8 @@ def parse():
                     help="DICE denoising-step loop: reuse fraction and time per step under three policies")
     ap.add_argument("--des-fit", action="store_true",
                     help="fit the DES per-expert latency model f(c) = a*c + b on the streaming kernels")
+    ap.add_argument("--rho", type=float, default=0.0,
+                    help="with --des-fit: tokens of a block correlate by rho (shared component); 0 = independent")
     ap.add_argument("--dense", action="store_true",
                     help="the grouped GEMM kernels on dense single-expert problems, with torch.matmul on the same "
                          "shapes for context")
@@ -105,12 +107,14 @@ def des_fit(args):
     At N = 32 each DES-Seq block is also set against DES-Vote with a core of the same size, and
     every block reports its routing fidelity against vanilla top-8 (4.4): the cosine similarity of
     the per-expert hit counts, and the share of the vanilla top-8 routing mass the chosen experts
-    keep. Prints one JSON line per block and one with the fit."""
+    keep. With --rho the block's tokens share a component (x_i = sqrt(rho) z + sqrt(1 - rho) e_i), a
+    stand-in for the coupled tokens of one decoding block that gives vanilla routing fewer distinct
+    experts. Prints one JSON line per block and one with the fit."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_gemm_amd as moe
-    from synth import WORKLOADS, gen_layer_inputs
+    from synth import WORKLOADS, gen_coupled_tokens, gen_layer_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -125,7 +129,11 @@ def des_fit(args):
         t = {"w_router": up(inp.bits["w_router.0"]), "w1": up(inp.bits["w1.0"]), "w2": up(inp.bits["w2.0"]),
              "w3": up(inp.bits["w3.0"])}
         copies.append((t, moe.weights_struct(t)))
-    x_all = up(inp.bits["x"])
+    if args.rho > 0.0:
+        _, xbits = gen_coupled_tokens(np.random.default_rng(7), base.S, base.d, args.rho)
+        x_all = up(xbits)
+    else:
+        x_all = up(inp.bits["x"])
     stream = torch.cuda.current_stream()
     rows, experts, times = [], [], []
     vanilla_hits = {}
@@ -187,7 +195,8 @@ def des_fit(args):
     pred = A @ coef
     d, f = base.d, base.f
     bytes_per_expert = 3 * d * f * 2
-    print(json.dumps({"fit": "stream_us = a*rows + b*experts + c0", "a_us_per_row": round(float(coef[0]), 4),
+    print(json.dumps({"fit": "stream_us = a*rows + b*experts + c0", "rho": args.rho,
+                      "a_us_per_row": round(float(coef[0]), 4),
                       "b_us_per_expert": round(float(coef[1]), 4), "c0_us": round(float(coef[2]), 3),
                       "max_abs_residual_us": round(float(np.abs(pred - np.asarray(times)).max()), 3),
                       "blocks": len(rows), "bytes_per_expert": bytes_per_expert,

@@ -113,6 +113,18 @@ def gen_tensor(rng: np.random.Generator, shape, std: float, dtype: str):
     return a, None
 
 
+def gen_coupled_tokens(rng: np.random.Generator, n: int, d: int, rho: float):
+    """A decode block of n bf16 tokens that share part of their content: x_i = sqrt(rho) * z +
+    sqrt(1 - rho) * e_i, with z and every e_i drawn N(0, I_d), so each token is N(0, I_d) and any two
+    correlate by rho (a stand-in for the semantically coupled tokens of one parallel-decoding
+    block). rho = 0 gives independent tokens. Returns (values float32, bf16 bits)."""
+    z = rng.standard_normal(size=(1, d), dtype=np.float32)
+    e = rng.standard_normal(size=(n, d), dtype=np.float32)
+    a = np.float32(np.sqrt(rho)) * z + np.float32(np.sqrt(1.0 - rho)) * e
+    bits, vals = bf16_rne(a)
+    return vals, bits
+
+
 @dataclass
 class LayerInputs:
     """Values are float32 arrays holding exactly the stored (bf16 or fp32) numbers.
