@@ -40,6 +40,11 @@
  *     negative moe_status and launches nothing on an argument error. No C++ exception crosses
  *     the ABI. Calls that overlap on one stream are ordered; calls on different streams that
  *     share a workspace race.
+ *   - An empty batch (desc->S == 0) is valid. It reads no token array, which may then be NULL, and
+ *     needs no workspace. moe_route and moe_layer_forward then only set the routing's
+ *     per-expert counts and offsets, n_rows and capacity to 0, DES votes to 0 and DES core slots
+ *     to -1 (moe_route needs `routing` for that; moe_layer_forward takes NULL). The other calls
+ *     do nothing.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -81,7 +86,7 @@ typedef enum { MOE_TOKEN_CHOICE = 0, MOE_EXPERT_CHOICE = 1, MOE_DES_VOTE = 2, MO
 /* Layer description [host]. Routed expert ids: [0, E_heavy) heavy, then n_identity identity,
  * n_zero zero and n_const constant experts; E_r = E_heavy + n_identity + n_zero + n_const. */
 typedef struct {
-  int32_t S, d, d_ff;           /* tokens, model dim, expert hidden dim                           */
+  int32_t S, d, d_ff;           /* tokens (0: an empty batch), model dim, expert hidden dim      */
   int32_t E_heavy, n_identity, n_zero, n_const;
   int32_t n_shared;             /* always-on experts, weight 1                                     */
   int32_t dtype;                /* moe_dtype                                                       */

@@ -88,7 +88,7 @@ bool is_des(const moe_desc* d) { return d->mode == MOE_DES_VOTE || d->mode == MO
 moe_status make_plan(const moe_desc* d, Plan* p) {
   if (!d) return MOE_EINVAL;
   if (d->flags & ~kKnownFlags) return MOE_EINVAL;
-  if (d->S < 1 || d->d < 1 || d->E_heavy < 0 || d->n_identity < 0 || d->n_zero < 0 || d->n_const < 0 ||
+  if (d->S < 0 || d->d < 1 || d->E_heavy < 0 || d->n_identity < 0 || d->n_zero < 0 || d->n_const < 0 ||
       d->n_shared < 0)
     return MOE_EINVAL;
   if (d->dtype != MOE_BF16 && d->dtype != MOE_F32) return MOE_EINVAL;
@@ -107,7 +107,7 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
     if (!std::isfinite(d->capacity_factor) || d->capacity_factor <= 0.f) return MOE_EINVAL;
     const double c = std::floor((double)d->capacity_factor * (double)d->S / (double)E_r);
     const int64_t C = (int64_t)std::min<double>((double)d->S, c);
-    if (C < 1) return MOE_EINVAL;
+    if (C < 1 && d->S > 0) return MOE_EINVAL;   // no tokens: no capacity either
     p->C = (int)C;
     p->k_eff = 0;
     p->R_max = E_r * C;
@@ -474,6 +474,25 @@ moe_status do_combine(const moe_desc* d, const Plan& p, const void* x, const moe
   return after_launch(launch_combine(a, st), d, st);
 }
 
+// A call with no tokens routes nothing: the per-expert counts and offsets, the row count and the
+// capacity become 0, the DES votes 0 and the core slots -1. Arrays of S rows are not touched (they
+// may be null).
+moe_status empty_routing(const moe_desc* d, const Plan& p, const moe_routing* r, hipStream_t st) {
+  if (!r) return MOE_OK;
+  if (!r->counts || !r->offsets || !r->n_rows) return MOE_EINVAL;
+  const size_t E = (size_t)p.E_r;
+  MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->counts, 0u, E, st), d, st));
+  MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->offsets, 0u, E + 1, st), d, st));
+  MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->n_rows, 0u, 1, st), d, st));
+  if (r->capacity) MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->capacity, 0u, 1, st), d, st));
+  if (is_des(d)) {
+    if (r->votes) MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->votes, 0u, E, st), d, st));
+    const size_t ncore = d->mode == MOE_DES_SEQ ? E : (size_t)d->m_core;
+    if (r->core) MOE_TRY(after_launch(launch_fill_u32((uint32_t*)r->core, 0xFFFFFFFFu, ncore, st), d, st));
+  }
+  return MOE_OK;
+}
+
 moe_status check_weights(const moe_desc* d, const moe_weights* w, bool need_router) {
   if (!w) return MOE_EINVAL;
   if (need_router && !w->w_router) return MOE_EINVAL;
@@ -497,6 +516,7 @@ moe_status moe_route(const moe_desc* desc, const float* logits, moe_routing* rou
                      void* stream) {
   Plan p;
   MOE_TRY(make_plan(desc, &p));
+  if (desc->S == 0) return routing ? empty_routing(desc, p, routing, (hipStream_t)stream) : MOE_EINVAL;
   if (!logits) return MOE_EINVAL;
   MOE_TRY(check_routing(desc, routing));
   MOE_TRY(check_ws(p, ws, ws_bytes));
@@ -506,6 +526,7 @@ moe_status moe_route(const moe_desc* desc, const float* logits, moe_routing* rou
 moe_status moe_dispatch(const moe_desc* desc, const void* x, const moe_routing* routing, void* x_perm, void* stream) {
   Plan p;
   MOE_TRY(make_plan(desc, &p));
+  if (desc->S == 0) return MOE_OK;
   if (!x || !x_perm || !routing || !routing->row_token || !routing->n_rows) return MOE_EINVAL;
   return after_launch(launch_gather(desc->dtype, x, routing->row_token, routing->n_rows, x_perm, (int)p.R_max,
                                     desc->d, (hipStream_t)stream),
@@ -517,8 +538,9 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const void* x_per
                           void* stream) {
   Plan p;
   MOE_TRY(make_plan(desc, &p));
-  if (!x) return MOE_EINVAL;
   MOE_TRY(check_weights(desc, weights, false));
+  if (desc->S == 0) return MOE_OK;
+  if (!x) return MOE_EINVAL;
   if (desc->E_heavy > 0 && (!routing || !routing->offsets || !routing->row_token || !y_perm)) return MOE_EINVAL;
   if (desc->n_shared > 0 && !y_shared) return MOE_EINVAL;
   MOE_TRY(check_ws(p, ws, ws_bytes));
@@ -530,6 +552,7 @@ moe_status moe_combine(const moe_desc* desc, const void* x, const moe_routing* r
                        void* stream) {
   Plan p;
   MOE_TRY(make_plan(desc, &p));
+  if (desc->S == 0) return MOE_OK;
   if (!x || !y || !routing) return MOE_EINVAL;
   if (desc->mode == MOE_EXPERT_CHOICE) {
     if (!routing->token_off || !routing->token_list || !routing->row_w) return MOE_EINVAL;
@@ -548,9 +571,10 @@ moe_status moe_layer_forward(const moe_desc* desc, const void* x, const moe_weig
                              void* ws, size_t ws_bytes, void* stream) {
   Plan p;
   MOE_TRY(make_plan(desc, &p));
-  if (!x || !y) return MOE_EINVAL;
   if (desc->flags & MOE_F_INPUT_PROBS) return MOE_EINVAL;
   MOE_TRY(check_weights(desc, weights, true));
+  if (desc->S == 0) return empty_routing(desc, p, routing, (hipStream_t)stream);
+  if (!x || !y) return MOE_EINVAL;
   if (desc->reuse_tau > 0.f && !cache) return MOE_EINVAL;
   MOE_TRY(check_ws(p, ws, ws_bytes));
   moe_routing internal;

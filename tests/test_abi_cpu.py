@@ -69,7 +69,7 @@ def _desc(**kw):
 
 
 INVALID = [
-    dict(k=0), dict(k=9), dict(S=0), dict(d=0), dict(E_heavy=-1), dict(dtype=7), dict(act=5), dict(mode=4),
+    dict(k=0), dict(k=9), dict(S=-1), dict(d=0), dict(E_heavy=-1), dict(dtype=7), dict(act=5), dict(mode=4),
     dict(d_ff=0), dict(reuse_tau=-0.5), dict(reuse_tau=float("nan")), dict(flags=0x1000),
     dict(flags=moe.MOE_F_FORCE_TILED | moe.MOE_F_FORCE_STREAM),
     dict(mode=moe.MOE_DES_VOTE, m_core=0, vote_k=8), dict(mode=moe.MOE_DES_VOTE, m_core=9, vote_k=2),
@@ -110,6 +110,25 @@ def test_unsupported_descriptors(kw):
     st = moe.moe_layer_forward(d, FAKE, moe.MoeWeights(*([FAKE] * 8)), None, None, None, FAKE, None, FAKE, FAKE,
                                1 << 40, stream=0, raise_on_error=False)
     assert st == moe.MOE_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["dit_moe_xl", "ec_dit", "des_vote_b025", "des_seq", "mmoe"])
+def test_empty_batch_is_valid_and_launches_nothing(name):
+    """S = 0 is a valid description in every mode (expert choice included, whose capacity is then 0).
+    Without routing arrays the layer has nothing to write, so it returns at once, with null token
+    arrays and no workspace (no HIP call is made: this runs without a GPU)."""
+    d = moe.desc_from_spec(WORKLOADS[name].replace(S=0))
+    assert moe.moe_workspace_bytes(d) >= 256
+    w = moe.MoeWeights(*([FAKE] * 8))
+    assert moe.moe_layer_forward(d, None, w, None, None, None, FAKE, None, None, None, 0, stream=0,
+                                 raise_on_error=False) == moe.MOE_OK
+    assert moe.moe_dispatch(d, None, moe.MoeRouting(), None, stream=0, raise_on_error=False) == moe.MOE_OK
+    assert moe.moe_combine(d, None, moe.MoeRouting(), None, None, FAKE, FAKE, None, None, stream=0,
+                           raise_on_error=False) == moe.MOE_OK
+    assert moe.moe_expert_ffn(d, None, None, moe.MoeRouting(), w, None, None, None, 0, stream=0,
+                              raise_on_error=False) == moe.MOE_OK
+    # moe_route writes the routing's counts; without routing arrays it is an argument error
+    assert moe.moe_route(d, None, moe.MoeRouting(), None, 0, stream=0, raise_on_error=False) == moe.MOE_EINVAL
 
 
 def test_null_pointers_and_workspace():

@@ -247,6 +247,44 @@ def test_mmoe_stack_reduced():
     _stack_case(WORKLOADS["mmoe"].replace(S=600))
 
 
+@pytest.mark.parametrize("name", ["dit_moe_xl", "ec_dit", "des_vote_b025", "des_seq", "mmoe"])
+def test_empty_batch_resets_routing(name):
+    """S = 0 routes nothing: moe_layer_forward and moe_route set the per-expert counts and offsets,
+    n_rows and the capacity to 0, DES votes to 0 and the DES core slots to -1, with null token
+    arrays and no workspace."""
+    spec = WORKLOADS[name].replace(S=4, n_layers=1)
+    say(f"empty batch {name}")
+    wt = upload_layer(gen_layer_inputs(spec))
+    rb = moe.alloc_routing(moe.desc_from_spec(spec))
+    d0 = moe.desc_from_spec(spec.replace(S=0))
+
+    def garbage():
+        for t in rb.tensors.values():
+            t.fill_(7)
+
+    def check():
+        torch.cuda.synchronize()
+        g = {k: v.cpu() for k, v in rb.tensors.items()}
+        assert int(g["counts"].abs().sum()) == 0 and int(g["offsets"].abs().sum()) == 0
+        assert int(g["n_rows"][0]) == 0
+        if "capacity" in g:
+            assert int(g["capacity"][0]) == 0
+        if spec.mode in ("des", "des_seq"):
+            assert float(g["votes"].abs().sum()) == 0.0
+            ncore = spec.m_core if spec.mode == "des" else spec.E_routed
+            assert bool((g["core"][:ncore] == -1).all())
+        # arrays of S rows are left alone
+        assert bool((g["topk_idx"] == 7).all()) if "topk_idx" in g else True
+
+    garbage()
+    assert moe.moe_layer_forward(d0, None, moe.weights_struct(wt), None, None, rb.struct, None, None, None, None,
+                                 0) == moe.MOE_OK
+    check()
+    garbage()
+    assert moe.moe_route(d0, None, rb.struct, None, 0) == moe.MOE_OK
+    check()
+
+
 FOUR_CALL_CASES = {
     # grouped GEMMs, then the combine kernel
     "dit_moe_xl": (WORKLOADS["dit_moe_xl"].replace(S=513), 0, False, False),

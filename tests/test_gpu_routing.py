@@ -55,6 +55,9 @@ def _check_permutation(spec, got, idx, reuse=None):
 TC_CASES = [
     # S, E_heavy, n_id, n_zero, n_const, k
     (1000, 8, 0, 0, 0, 2),
+    # the library's limits: 256 routed experts, k = 16 (one-workgroup kernel at S * E_r = 8192)
+    (32, 256, 0, 0, 0, 16),
+    (300, 256, 0, 0, 0, 16),
     (777, 16, 1, 1, 1, 2),
     (333, 64, 0, 0, 0, 8),
     (129, 200, 0, 0, 0, 16),
@@ -111,6 +114,7 @@ def test_tc_route_bitexact_on_probs_with_reuse(renorm, S):
 EC_CASES = [
     # S, E, f_c
     (8192, 32, 2.0),
+    (1024, 256, 2.0),   # 256 experts (the limit), C = 8
     (1000, 7, 1.3),
     (50, 4, 8.0),
     (2049, 64, 1.0),
@@ -153,6 +157,7 @@ def test_ec_route_on_logits_full_size():
 DES_CASES = [
     # N, E, K, M, k
     (32, 64, 8, 16, 8),
+    (32, 256, 16, 64, 16),   # the limits: 256 experts, k = 16
     (32, 64, 8, 32, 8),
     (6, 10, 3, 4, 2),
     (100, 19, 4, 3, 8),
@@ -213,6 +218,7 @@ def test_des_route_on_logits_full_size():
 DES_SEQ_CASES = [
     # N, E, k_seq, k
     (32, 64, 1, 8),
+    (32, 256, 4, 16),   # the limits: 256 experts, k = 16
     (32, 64, 2, 8),
     (32, 64, 4, 8),
     (6, 10, 1, 4),      # small union: |core| may fall below k (empty slots)
