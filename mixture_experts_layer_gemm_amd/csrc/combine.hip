@@ -69,94 +69,159 @@ hipError_t launch_gather(int dtype, const void* x, const int32_t* row_token, con
   return hipGetLastError();
 }
 
-// KM: an upper bound on k (2, 4, 8 or 16), which sizes the per-slot registers
+// KM: an upper bound on k (2, 4, 8 or 16), which sizes the per-slot registers.
+// Latency: every load that does not depend on another one is issued first, together (the reuse
+// flag, the slots' expert / weight / row, the shared-expert and residual rows), then the rows the
+// slots name, all of them together; so a call with few tokens (a decode block) waits for two
+// rounds of memory latency instead of one or two per slot.
 template <typename T, bool EC, int KM>
 __global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
-  constexpr int GRP = KM < 4 ? KM : 4;   // slots whose rows are loaded together
   const int cpr = a.d >> 3;
   const size_t total = (size_t)a.S * cpr;
   const T* x = (const T*)a.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
     const int s = (int)(i / cpr);
     const int c0 = (int)(i - (size_t)s * cpr) * 8;
-    float routed[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    float v[8];
-    const bool reused = a.reuse && a.reuse[s];
-    if (reused) {
-      load8<T>((const T*)a.cache + (size_t)s * a.d + c0, routed);
-    } else if (!EC) {
-      // the slots' metadata first, then their rows GRP at a time, added in slot order: the loads of
-      // a group are in flight together instead of one dependent pair per slot
-      int src_kind[KM], src_row[KM];
-      float src_w[KM];
+    const size_t row = (size_t)s * a.d + c0;
+    // independent loads. The reuse flag comes first, so waiting for it leaves the others in flight.
+    // Without a reuse mask, a byte of another array this call reads stands in: a load with no
+    // branch around it is not waited for until its value is used.
+    const uint8_t* fl = a.reuse ? a.reuse + s : reinterpret_cast<const uint8_t*>(EC ? a.token_off : a.topk_idx);
+    const uint8_t rflag = *fl;
+    int e[KM], tr[KM];
+    float w[KM];
+    int q0 = 0, q1 = 0;   // expert choice: the token's entries in the token CSR
+    if (EC) {
+      q0 = a.token_off[s];
+      q1 = a.token_off[s + 1];
+    } else {
 #pragma unroll
       for (int j = 0; j < KM; ++j) {
-        src_kind[j] = 0;   // 0: nothing (also an empty slot), 1: routed row, 2: x, 3: constant row
-        src_row[j] = 0;
-        src_w[j] = 0.f;
-        if (j < a.k) {
-          const int e = a.topk_idx[(size_t)s * a.k + j];   // -1: an empty DES-Seq slot
-          src_w[j] = a.topk_w[(size_t)s * a.k + j];
-          int l = e - a.E_heavy;
-          if (e < 0) {
-            // nothing
-          } else if (l < 0) {
-            src_kind[j] = 1;
-            src_row[j] = a.token_rows[(size_t)s * a.k + j];
-          } else if (l < a.n_identity) {
-            src_kind[j] = 2;
-          } else if ((l -= a.n_identity) >= a.n_zero) {
-            src_kind[j] = 3;
-            src_row[j] = l - a.n_zero;
-          }
+        const size_t o = (size_t)s * a.k + min(j, a.k - 1);   // slots past k re-read the last one
+        e[j] = a.topk_idx[o];                                 // -1: an empty DES-Seq slot
+        w[j] = a.topk_w[o];
+        tr[j] = a.token_rows[o];
+      }
+    }
+    // the shared-expert and residual rows as raw 16-byte pieces, converted at the end
+    constexpr int LW = sizeof(T) == 4 ? 2 : 1;   // 16-byte pieces of 8 elements of T
+    uint4 rsh[2], rres[LW];
+    if (a.y_shared) {
+      const uint4* p = reinterpret_cast<const uint4*>(a.y_shared + row);
+      rsh[0] = p[0];
+      rsh[1] = p[1];
+    }
+    if (a.residual) {
+      const uint4* p = reinterpret_cast<const uint4*>((const T*)a.residual + row);
+#pragma unroll
+      for (int h = 0; h < LW; ++h) rres[h] = p[h];
+    }
+    const bool reused = a.reuse && rflag != 0;
+
+    float routed[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (reused) {
+      load8<T>((const T*)a.cache + row, routed);
+    } else if (!EC) {
+      // each slot's source row: 0 nothing (a slot past k, an empty slot, a zero expert), 1 a routed
+      // row of y_perm, 2 x (identity), 3 a constant expert's vector
+      int kind[KM];
+      const T* src[KM];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        const int l = e[j] - a.E_heavy;
+        const int lc = l - a.n_identity - a.n_zero;   // constant expert index
+        kind[j] = j >= a.k || e[j] < 0 ? 0 : l < 0 ? 1 : l < a.n_identity ? 2 : lc >= 0 ? 3 : 0;
+        src[j] = kind[j] == 3 ? (const T*)a.const_vec + (size_t)lc * a.d + c0 : x + row;
+      }
+      // raw 16-byte pieces first, into registers of their own per kind of source (a load whose
+      // destination another branch also writes would have to wait for that one), converted after
+      uint4 rp[KM][2], rx[KM][LW];
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (kind[j] == 1) {
+          const uint4* p = reinterpret_cast<const uint4*>(a.y_perm + (size_t)tr[j] * a.d + c0);
+          rp[j][0] = p[0];
+          rp[j][1] = p[1];
+        }
+        if (kind[j] >= 2) {
+          const uint4* p = reinterpret_cast<const uint4*>(src[j]);
+#pragma unroll
+          for (int h = 0; h < LW; ++h) rx[j][h] = p[h];
         }
       }
+      // added in slot order
 #pragma unroll
-      for (int j0 = 0; j0 < KM; j0 += GRP) {
-        if (j0 < a.k) {
-          float vv[GRP][8];
-#pragma unroll
-          for (int jj = 0; jj < GRP; ++jj) {
-            const int j = j0 + jj;
-            if (src_kind[j] == 1) load8<float>(a.y_perm + (size_t)src_row[j] * a.d + c0, vv[jj]);
-            else if (src_kind[j] == 2) load8<T>(x + (size_t)s * a.d + c0, vv[jj]);
-            else if (src_kind[j] == 3) load8<T>((const T*)a.const_vec + (size_t)src_row[j] * a.d + c0, vv[jj]);
+      for (int j = 0; j < KM; ++j) {
+        if (kind[j] != 0) {
+          float vv[8];
+          if (kind[j] == 1) {
+            unpack16(rp[j][0], vv, float());
+            unpack16(rp[j][1], vv + 4, float());
+          } else if (sizeof(T) == 4) {
+            unpack16(rx[j][0], vv, float());
+            unpack16(rx[j][LW - 1], vv + 4, float());
+          } else {
+            unpack16(rx[j][0], vv, bf16_t());
           }
 #pragma unroll
-          for (int jj = 0; jj < GRP; ++jj) {
-            if (src_kind[j0 + jj] != 0) {
-#pragma unroll
-              for (int q = 0; q < 8; ++q) routed[q] += src_w[j0 + jj] * vv[jj][q];
-            }
-          }
+          for (int q = 0; q < 8; ++q) routed[q] += w[j] * vv[q];
         }
       }
     } else {
-      const int q0 = a.token_off[s], q1 = a.token_off[s + 1];
-      for (int qq = q0; qq < q1; ++qq) {
-        const int r = a.token_list[qq];
-        const float w = a.row_w[r];
-        load8<float>(a.y_perm + (size_t)r * a.d + c0, v);
+      // the experts that chose the token, four entries at a time: their rows are in flight together
+      constexpr int U = 4;
+      for (int qb = q0; qb < q1; qb += U) {
+        int r[U];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) routed[q] += w * v[q];
+        for (int u = 0; u < U; ++u) r[u] = a.token_list[min(qb + u, q1 - 1)];
+        float wr[U];
+        uint4 rp[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          wr[u] = a.row_w[r[u]];
+          const uint4* p = reinterpret_cast<const uint4*>(a.y_perm + (size_t)r[u] * a.d + c0);
+          rp[u][0] = p[0];
+          rp[u][1] = p[1];
+        }
+        // (the scheduler would otherwise interleave the loads with their uses to save registers)
+        __builtin_amdgcn_sched_barrier(0);
+        // entries past the last re-read it and add it with weight 0 (no branch around the use, so
+        // the compiler keeps the four loads together)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float wu = qb + u < q1 ? wr[u] : 0.f;
+          float v[8];
+          unpack16(rp[u][0], v, float());
+          unpack16(rp[u][1], v + 4, float());
+#pragma unroll
+          for (int q = 0; q < 8; ++q) routed[q] += wu * v[q];
+        }
       }
     }
-    if (a.cache && !reused) store8<T>((T*)a.cache + (size_t)s * a.d + c0, routed);
+    if (a.cache && !reused) store8<T>((T*)a.cache + row, routed);
     float out[8];
     if (a.y_shared) {
-      load8<float>(a.y_shared + (size_t)s * a.d + c0, out);
+      float sh[8];
+      unpack16(rsh[0], sh, float());
+      unpack16(rsh[1], sh + 4, float());
 #pragma unroll
-      for (int q = 0; q < 8; ++q) out[q] += routed[q];
+      for (int q = 0; q < 8; ++q) out[q] = sh[q] + routed[q];
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) out[q] = routed[q];
     }
     if (a.residual) {
-      load8<T>((const T*)a.residual + (size_t)s * a.d + c0, v);
+      float res[8];
+      if (sizeof(T) == 4) {
+        unpack16(rres[0], res, float());
+        unpack16(rres[LW - 1], res + 4, float());
+      } else {
+        unpack16(rres[0], res, bf16_t());
+      }
 #pragma unroll
-      for (int q = 0; q < 8; ++q) out[q] += v[q];
+      for (int q = 0; q < 8; ++q) out[q] += res[q];
     }
-    store8<T>((T*)a.y + (size_t)s * a.d + c0, out);
+    store8<T>((T*)a.y + row, out);
   }
 }
 

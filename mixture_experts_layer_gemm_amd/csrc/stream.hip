@@ -22,24 +22,40 @@
 
 namespace moe {
 
-// The slot-th expert (ascending id) with at least one row, or -1. s_e: one int of LDS to pass it on.
-__device__ __forceinline__ int locate_active(const GemmProblem& P, int slot, int* s_e) {
+// The slot-th expert (ascending id) with at least one row, with its first row and row count
+// (e = -1, cnt = 0 past the last one). The offsets read to find it give those too, so the
+// workgroup waits for one round of memory latency, not two. sh: three ints of LDS to pass them on.
+struct ActiveExpert {
+  int e, beg, cnt;
+};
+__device__ __forceinline__ ActiveExpert locate_active(const GemmProblem& P, int slot, int* sh) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int carry = 0, found = -1;
+    int carry = 0, found = -1, beg = 0, cnt = 0;
     for (int g0 = 0; g0 < P.G && found < 0; g0 += 64) {
       const int gi = g0 + lane;
-      const bool act = gi < P.G && P.offsets[gi + 1] > P.offsets[gi];
+      const int o0 = gi < P.G ? P.offsets[gi] : 0;
+      const int o1 = gi < P.G ? P.offsets[gi + 1] : 0;
+      const bool act = gi < P.G && o1 > o0;
       const uint64_t m = __ballot(act);
       const int before = carry + __popcll(m & lanemask_lt());
       const uint64_t hit = __ballot(act && before == slot);
-      if (hit) found = g0 + __ffsll((unsigned long long)hit) - 1;
+      if (hit) {
+        const int l = __ffsll((unsigned long long)hit) - 1;
+        found = g0 + l;
+        beg = __shfl(o0, l, 64);
+        cnt = __shfl(o1, l, 64) - beg;
+      }
       carry += __popcll(m);
     }
-    if (lane == 0) *s_e = found;
+    if (lane == 0) {
+      sh[0] = found;
+      sh[1] = beg;
+      sh[2] = cnt;
+    }
   }
   __syncthreads();
-  return *s_e;
+  return ActiveExpert{sh[0], sh[1], sh[2]};
 }
 
 // G (16-column groups) x SL (K slices) waves per workgroup
@@ -51,13 +67,11 @@ __global__ __launch_bounds__(64 * G * SL) void k_stream_gemm(GemmProblem la_p) {
   constexpr bool SWIGLU = (ACT == ACT_SWIGLU) && (KIND == GEMM_UP);
   constexpr int NACC = SWIGLU ? 4 : 2;   // floatx4 accumulators per lane: 2 token groups (x gate)
   __shared__ floatx4_t s_red[SL - 1][G][NACC][64];
-  __shared__ int s_e;
+  __shared__ int s_act[3];
   const GemmProblem& P = la_p;
-  const int e = locate_active(P, blockIdx.y, &s_e);
-  if (e < 0) return;
-  const int beg = P.offsets[e];
-  const int cnt = P.offsets[e + 1] - beg;
-  if (cnt <= 0) return;
+  const ActiveExpert ae = locate_active(P, blockIdx.y, s_act);
+  const int e = ae.e, beg = ae.beg, cnt = ae.cnt;
+  if (e < 0 || cnt <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cg = wave % G, ks = wave / G;
   const int fr = lane & 15, fg = lane >> 4;
@@ -200,14 +214,14 @@ __global__ __launch_bounds__(256) void k_stream_ring(GemmProblem la_p) {
   static_assert(4 * GRP * NB * 64 * 16 <= 4 * D * SLOT, "reduction fits in the ring");
   __shared__ __attribute__((aligned(16))) uint8_t ring[4][D][SLOT];
   const GemmProblem& P = la_p;
-  // the expert comes through the ring's first word (the ring may fill all of LDS); every thread
-  // has read it before any load into the ring is issued
-  const int e = __builtin_amdgcn_readfirstlane(locate_active(P, blockIdx.y, reinterpret_cast<int*>(&ring[0][0][0])));
+  // the expert comes through the ring's first words (the ring may fill all of LDS); every thread
+  // has read them before any load into the ring is issued
+  const ActiveExpert ae = locate_active(P, blockIdx.y, reinterpret_cast<int*>(&ring[0][0][0]));
   __syncthreads();
-  if (e < 0) return;
-  const int beg = P.offsets[e];
-  const int cnt = P.offsets[e + 1] - beg;
-  if (cnt <= 0) return;
+  const int e = __builtin_amdgcn_readfirstlane(ae.e);
+  const int beg = __builtin_amdgcn_readfirstlane(ae.beg);
+  const int cnt = __builtin_amdgcn_readfirstlane(ae.cnt);
+  if (e < 0 || cnt <= 0) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int fr = lane & 15, fg = lane >> 4;
