@@ -559,6 +559,7 @@ constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallMaxSE = 8192;     // S * E_r: keys and probabilities kept in LDS
 constexpr int kSmallMaxPairs = 4096;  // S * k
 constexpr int kSmallMaxS = 2048;
+static_assert(kSmallMaxPairs % kSmallThreads == 0, "whole rounds of pairs");
 
 bool route_small_supported(int S, int E_r, int k) {
   return S >= 1 && S <= kSmallMaxS && (int64_t)S * E_r <= kSmallMaxSE && (int64_t)S * k <= kSmallMaxPairs &&
@@ -814,27 +815,42 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     lds_barrier();
   }
   // weights: p, or p over the sum of the chosen p in slot order; DES-Seq slots past min(k, |core|)
-  // hold expert -1 and weight 0
-  for (int s = tid; s < S; s += kSmallThreads) {
-    float denom = 1.f;
-    if (a.renorm) {
-      float t = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < kk; ++j) t += s_w[s * ks + j];
-      denom = t;
+  // hold expert -1 and weight 0. One thread per (token, slot) pair, each adding its token's chosen
+  // p itself in slot order; every pair is read before any is rewritten (a token's slots may span
+  // two rounds of the workgroup).
+  {
+    constexpr int RMAX = kSmallMaxPairs / kSmallThreads;
+    const int P = S * ks;
+    float wv[RMAX];
+    int ev[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const int p = r * kSmallThreads + tid;
+      wv[r] = 0.f;
+      ev[r] = -1;
+      if (p < P) {
+        const int s = p / ks, j = p - s * ks;
+        if (j < kk) {
+          ev[r] = s_idx[p];
+          wv[r] = s_w[p];
+          if (a.renorm) {
+            float t = 0.f;
+            for (int jj = 0; jj < kk; ++jj) t += s_w[s * ks + jj];
+            wv[r] = wv[r] / t;
+          }
+        }
+      }
     }
-#pragma unroll 4
-    for (int j = 0; j < kk; ++j) {
-      const float wj = a.renorm ? s_w[s * ks + j] / denom : s_w[s * ks + j];
-      s_w[s * ks + j] = wj;
-      a.topk_idx[(size_t)s * ks + j] = s_idx[s * ks + j];
-      a.topk_w[(size_t)s * ks + j] = wj;
-    }
-    for (int j = kk; j < ks; ++j) {
-      s_idx[s * ks + j] = -1;
-      s_w[s * ks + j] = 0.f;
-      a.topk_idx[(size_t)s * ks + j] = -1;
-      a.topk_w[(size_t)s * ks + j] = 0.f;
+    lds_barrier();
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const int p = r * kSmallThreads + tid;
+      if (p < P) {
+        s_idx[p] = ev[r];
+        s_w[p] = wv[r];
+        a.topk_idx[p] = ev[r];
+        a.topk_w[p] = wv[r];
+      }
     }
   }
   lds_barrier();
