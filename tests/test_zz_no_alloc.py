@@ -50,3 +50,47 @@ def test_noalloc_matches_workspace_entry_point(first, second):
         for key in ("topk_idx", "topk_w", "counts", "offsets", "row_token", "n_rows"):
             assert torch.equal(r0[key], r1[key]), key
         say(f"  bit-identical: y {tuple(y0.shape)}, rows {int(r0['n_rows'][0])}")
+
+
+def test_noalloc_under_graph_capture():
+    """The callers it is for: a decode-block layer captured into a HIP graph through the entry point
+    that allocates nothing, replayed four times with eager calls of the same entry point (other
+    inputs, the same static scratch) between the replays; every replay equals the eager result."""
+    spec = WORKLOADS["des_vote_b025"]
+    desc = moe.desc_from_spec(spec)
+    bufs = []
+    for seed in (0, 1):
+        inp = gen_layer_inputs(spec, seed=seed)
+        x = dev_tensor(inp.x, inp.bits.get("x"), spec.dtype)
+        wt = upload_layer(inp)
+        bufs.append((x, wt, moe.weights_struct(wt), torch.empty_like(x), moe.alloc_routing(desc)))
+    (x, _, w, y, rb), (x2, _, w2, y2, rb2) = bufs
+    logits = torch.empty((spec.S, spec.E_routed), dtype=torch.float32, device="cuda")
+
+    def call(stream):
+        moe.moe_layer_forward_noalloc(desc, x, w, None, logits, rb.struct, None, x, y, stream=stream)
+
+    call(torch.cuda.current_stream().cuda_stream)   # eager reference (also sets up the scratch address)
+    torch.cuda.synchronize()
+    y_ref, l_ref = y.clone(), logits.clone()
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            call(side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    for rep in range(4):
+        y.fill_(0)
+        logits.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}: output differs from eager"
+        assert torch.equal(logits, l_ref), f"replay {rep}: logits differ from eager"
+        moe.moe_layer_forward_noalloc(desc, x2, w2, None, None, rb2.struct, None, x2, y2)
+        torch.cuda.synchronize()
+    say("  graph replays of the no-allocation entry point: bit-identical")
