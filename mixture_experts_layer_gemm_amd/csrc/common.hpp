@@ -120,7 +120,9 @@ __device__ __forceinline__ float gelu_erf(float z) {
   q = q * q;
   q = q * q;
   q = q * q;   // q^16; overflows to inf for large |z|, whose reciprocal is 0
-  return fmaf(-u, fast_rcp(q), fmaxf(z, 0.0f));
+  // max(z, 0) as a median of three (z, 0, the largest float): for finite z the same value, in one
+  // instruction where fmaxf takes two (it first quiets a possible signalling NaN)
+  return fmaf(-u, fast_rcp(q), __builtin_amdgcn_fmed3f(z, 0.0f, 3.402823466e38f));
 }
 // tanh form: 0.5 z (1 + tanh(u)) = z - z / (1 + e^{2u}), u = sqrt(2/pi) (z + 0.044715 z^3)
 __device__ __forceinline__ float gelu_tanh(float z) {
