@@ -71,6 +71,23 @@ def test_tiny_f32_layer_full_size():
     _layer_case(spec, flags=moe.MOE_F_FORCE_STREAM)
 
 
+F32_CASES = {
+    # every routing mode and expert kind in fp32 end to end (fp32 MFMA, register weight streaming)
+    "des_vote": (WORKLOADS["des_vote_b025"].replace(S=32, d=256, f=256, m_core=8, dtype="f32"), 0, False, False),
+    "des_seq": (WORKLOADS["des_seq"].replace(S=24, d=256, f=256, dtype="f32"), 0, False, False),
+    "ec": (WORKLOADS["ec_dit"].replace(S=300, d=128, f=256, E_heavy=8, dtype="f32"), 0, False, False),
+    "mmoe_light_shared": (WORKLOADS["mmoe"].replace(S=200, d=128, f=256, n_layers=1, dtype="f32"), 0, False, True),
+    "reuse_stream": (WORKLOADS["dit_moe_xl_reuse"].replace(S=96, d=128, f=256, reuse_tau=0.2, dtype="f32"),
+                     moe.MOE_F_FORCE_STREAM, True, False),
+}
+
+
+@pytest.mark.parametrize("name", list(F32_CASES))
+def test_f32_layer_modes(name):
+    spec, flags, with_cache, residual = F32_CASES[name]
+    _layer_case(spec, flags=flags, with_cache=with_cache, residual=residual)
+
+
 def test_dit_moe_xl_layer_reduced():
     spec = WORKLOADS["dit_moe_xl"].replace(S=700)
     _layer_case(spec)
