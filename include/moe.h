@@ -40,6 +40,9 @@
  *     negative moe_status and launches nothing on an argument error. No C++ exception crosses
  *     the ABI. Calls that overlap on one stream are ordered; calls on different streams that
  *     share a workspace race.
+ *   - Token rows (x, x_perm, residual, cache, y), expert outputs (y_perm, y_shared), weights and
+ *     constant vectors are read and written 16 bytes at a time: each must start on a 16-byte
+ *     boundary, or the call returns MOE_EINVAL.
  *   - An empty batch (desc->S == 0) is valid. It reads no token array, which may then be NULL, and
  *     needs no workspace. moe_route and moe_layer_forward then only set the routing's
  *     per-expert counts and offsets, n_rows and capacity to 0, DES votes to 0 and DES core slots

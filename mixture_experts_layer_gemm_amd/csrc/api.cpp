@@ -493,12 +493,18 @@ moe_status empty_routing(const moe_desc* d, const Plan& p, const moe_routing* r,
   return MOE_OK;
 }
 
+// Token rows, expert outputs and weights are read and written 16 bytes at a time (vector and
+// global->LDS loads), so every such buffer must start on a 16-byte boundary (null: not used).
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
 moe_status check_weights(const moe_desc* d, const moe_weights* w, bool need_router) {
   if (!w) return MOE_EINVAL;
   if (need_router && !w->w_router) return MOE_EINVAL;
   if (d->E_heavy > 0 && (!w->w1 || !w->w2 || (d->act == MOE_ACT_SWIGLU && !w->w3))) return MOE_EINVAL;
   if (d->n_shared > 0 && (!w->s_w1 || !w->s_w2 || (d->act == MOE_ACT_SWIGLU && !w->s_w3))) return MOE_EINVAL;
   if (d->n_const > 0 && !w->const_vec) return MOE_EINVAL;
+  for (const void* p : {w->w_router, w->w1, w->w2, w->w3, w->s_w1, w->s_w2, w->s_w3, w->const_vec})
+    if (!aligned16(p)) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -528,6 +534,7 @@ moe_status moe_dispatch(const moe_desc* desc, const void* x, const moe_routing* 
   MOE_TRY(make_plan(desc, &p));
   if (desc->S == 0) return MOE_OK;
   if (!x || !x_perm || !routing || !routing->row_token || !routing->n_rows) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(x_perm)) return MOE_EINVAL;
   return after_launch(launch_gather(desc->dtype, x, routing->row_token, routing->n_rows, x_perm, (int)p.R_max,
                                     desc->d, (hipStream_t)stream),
                       desc, (hipStream_t)stream);
@@ -541,6 +548,7 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const void* x_per
   MOE_TRY(check_weights(desc, weights, false));
   if (desc->S == 0) return MOE_OK;
   if (!x) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(x_perm) || !aligned16(y_perm) || !aligned16(y_shared)) return MOE_EINVAL;
   if (desc->E_heavy > 0 && (!routing || !routing->offsets || !routing->row_token || !y_perm)) return MOE_EINVAL;
   if (desc->n_shared > 0 && !y_shared) return MOE_EINVAL;
   MOE_TRY(check_ws(p, ws, ws_bytes));
@@ -554,6 +562,9 @@ moe_status moe_combine(const moe_desc* desc, const void* x, const moe_routing* r
   MOE_TRY(make_plan(desc, &p));
   if (desc->S == 0) return MOE_OK;
   if (!x || !y || !routing) return MOE_EINVAL;
+  for (const void* q : {x, (const void*)y_perm, (const void*)y_shared, const_vec, (const void*)cache, residual,
+                        (const void*)y})
+    if (!aligned16(q)) return MOE_EINVAL;
   if (desc->mode == MOE_EXPERT_CHOICE) {
     if (!routing->token_off || !routing->token_list || !routing->row_w) return MOE_EINVAL;
   } else {
@@ -575,6 +586,7 @@ moe_status moe_layer_forward(const moe_desc* desc, const void* x, const moe_weig
   MOE_TRY(check_weights(desc, weights, true));
   if (desc->S == 0) return empty_routing(desc, p, routing, (hipStream_t)stream);
   if (!x || !y) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(cache) || !aligned16(residual)) return MOE_EINVAL;
   if (desc->reuse_tau > 0.f && !cache) return MOE_EINVAL;
   MOE_TRY(check_ws(p, ws, ws_bytes));
   moe_routing internal;

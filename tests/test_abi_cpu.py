@@ -131,6 +131,30 @@ def test_empty_batch_is_valid_and_launches_nothing(name):
     assert moe.moe_route(d, None, moe.MoeRouting(), None, 0, stream=0, raise_on_error=False) == moe.MOE_EINVAL
 
 
+def test_misaligned_buffers_are_rejected():
+    """Buffers read or written 16 bytes at a time must start on a 16-byte boundary: a token array, an
+    expert-output array or a weight that does not gives MOE_EINVAL before any launch."""
+    d = moe.desc_from_spec(WORKLOADS["dit_moe_xl"])
+    bad = FAKE + 8
+    good_w = moe.MoeWeights(*([FAKE] * 8))
+    bad_w = moe.MoeWeights(*([FAKE] * 8))
+    bad_w.w1 = bad
+    ws = 1 << 40
+    def layer(x=FAKE, y=FAKE, w=good_w, residual=None):
+        return moe.moe_layer_forward(d, x, w, None, None, None, FAKE, residual, y, FAKE, ws, stream=0,
+                                     raise_on_error=False)
+    assert layer(x=bad) == moe.MOE_EINVAL
+    assert layer(y=bad) == moe.MOE_EINVAL
+    assert layer(residual=bad) == moe.MOE_EINVAL
+    assert layer(w=bad_w) == moe.MOE_EINVAL
+    r = moe.MoeRouting(*([FAKE] * 15))
+    assert moe.moe_dispatch(d, bad, r, FAKE, stream=0, raise_on_error=False) == moe.MOE_EINVAL
+    assert moe.moe_combine(d, FAKE, r, bad, FAKE, None, None, None, FAKE, stream=0,
+                           raise_on_error=False) == moe.MOE_EINVAL
+    assert moe.moe_expert_ffn(d, FAKE, None, r, good_w, FAKE, bad, FAKE, ws, stream=0,
+                              raise_on_error=False) == moe.MOE_EINVAL
+
+
 def test_null_pointers_and_workspace():
     d = _desc()
     w = moe.MoeWeights(*([FAKE] * 8))
