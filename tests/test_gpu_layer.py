@@ -302,6 +302,31 @@ def test_empty_batch_resets_routing(name):
     check()
 
 
+def test_des_with_full_cover_is_token_choice():
+    """Degenerate DES cases ("Dynamic Expert Sharing", 2.2-2.4): a DES-Vote core of every expert
+    (beta = 1), or a DES-Seq core built from each token's own top-k (k_seq = k), leaves every token its
+    plain top-k, so the layer equals token choice bit for bit (same streaming kernels)."""
+    base = WORKLOADS["des_vote_b025"]
+    tc = base.replace(mode="tc")
+    vote_all = base.replace(m_core=base.E_heavy)
+    seq_k = WORKLOADS["des_seq"].replace(vote_k=base.k)
+    inp = gen_layer_inputs(tc, seed=11)
+    x = dev_tensor(inp.x, inp.bits["x"], "bf16")
+    wt = upload_layer(inp)
+    outs = {}
+    for name, spec in (("tc", tc), ("vote_all", vote_all), ("seq_k", seq_k)):
+        y, logits, rb = run_layer(spec, x, wt, flags=moe.MOE_F_FORCE_STREAM)
+        outs[name] = (y, logits, routing_np(rb, spec))
+    y0, l0, g0 = outs["tc"]
+    for name in ("vote_all", "seq_k"):
+        y1, l1, g1 = outs[name]
+        say(f"  {name}: equal to token choice")
+        assert torch.equal(l0, l1)
+        assert np.array_equal(g0["topk_idx"], g1["topk_idx"]), name
+        assert np.array_equal(g0["topk_w"], g1["topk_w"]), name
+        assert torch.equal(y0, y1), name
+
+
 FOUR_CALL_CASES = {
     # grouped GEMMs, then the combine kernel
     "dit_moe_xl": (WORKLOADS["dit_moe_xl"].replace(S=513), 0, False, False),
