@@ -64,6 +64,8 @@ struct Plan {
   // workspace pieces (byte offsets)
   size_t o_blk = 0, o_filt = 0, o_pT = 0, o_tokrows = 0, o_tokcnt = 0;   // route scratch
   size_t o_logits = 0;                                                  // router output
+  int nsplit = 1;                                                       // router K splits
+  size_t o_rpart = 0;                                                   // their partial sums
   size_t o_rt = 0;                                                      // internal routing arrays
   size_t o_h = 0, o_hs = 0, o_yp = 0, o_ys = 0;                         // expert buffers
   size_t total = 0;
@@ -175,6 +177,9 @@ moe_status make_plan(const moe_desc* d, Plan* p) {
   p->o_tokrows = take(d->mode == MOE_EXPERT_CHOICE ? S * Er * 4 : 0);
   p->o_tokcnt = take(d->mode == MOE_EXPERT_CHOICE ? S * 4 : 0);
   p->o_logits = take(S * Er * 4);
+  // expert choice routes with its own kernels, which read finished logits
+  p->nsplit = d->mode == MOE_EXPERT_CHOICE ? 1 : router_splits(d->dtype == MOE_BF16 ? 0 : 1, d->S, d->d, E_r);
+  p->o_rpart = take(p->nsplit > 1 ? (size_t)p->nsplit * S * Er * 4 : 0);
   // internal routing arrays
   size_t r = 0;
   auto rt = [&](size_t bytes) {
@@ -263,8 +268,10 @@ moe_routing internal_routing(const Plan& p, const moe_desc* d, void* ws) {
   return r;
 }
 
+// keys: the logits (or given probabilities). From the layer call with p.nsplit > 1 they are still to
+// be formed from the router's partial sums (part) and prev, and written to keys.
 moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool input_probs, const moe_routing* r,
-                    void* ws, hipStream_t st) {
+                    void* ws, hipStream_t st, const float* part = nullptr, const float* prev = nullptr) {
   uint8_t* w = (uint8_t*)ws;
   if (d->mode == MOE_EXPERT_CHOICE) {
     ECArgs a{};
@@ -325,8 +332,19 @@ moe_status do_route(const moe_desc* d, const Plan& p, const float* keys, bool in
   q.token_rows = r->token_rows;
   q.n_rows = r->n_rows;
   q.blk_cnt = (int32_t*)(w + p.o_blk);
-  // small calls (a decode block, a tiny batch): routing and dispatch in one workgroup
-  if (!(d->flags & MOE_F_ROUTE_MULTI) && route_small_supported(d->S, p.E_r, p.k_eff)) return after_launch(launch_route_small(a, q, des, st), d, st);
+  // small calls (a decode block, a tiny batch): routing and dispatch in one workgroup, which also
+  // adds the router's K splits
+  if (!(d->flags & MOE_F_ROUTE_MULTI) && route_small_supported(d->S, p.E_r, p.k_eff)) {
+    if (part) {
+      a.part = part;
+      a.nsplit = p.nsplit;
+      a.prev = prev;
+      a.logits = const_cast<float*>(keys);
+    }
+    return after_launch(launch_route_small(a, q, des, st), d, st);
+  }
+  if (part)
+    MOE_TRY(after_launch(launch_router_sum(part, p.nsplit, prev, const_cast<float*>(keys), d->S * p.E_r, st), d, st));
   if (des) MOE_TRY(after_launch(launch_route_des(a, (float*)(w + p.o_filt), st), d, st));
   else MOE_TRY(after_launch(launch_route_topk(a, st), d, st));
   return after_launch(launch_permute(q, st), d, st);
@@ -599,9 +617,11 @@ moe_status moe_layer_forward(const moe_desc* desc, const void* x, const moe_weig
   hipStream_t st = (hipStream_t)stream;
   uint8_t* w = (uint8_t*)ws;
   float* logits = logits_out ? logits_out : (float*)(w + p.o_logits);
-  MOE_TRY(after_launch(launch_router(desc->dtype, x, weights->w_router, prev_logits, logits, desc->S, desc->d, p.E_r, st),
+  float* part = p.nsplit > 1 ? (float*)(w + p.o_rpart) : nullptr;
+  MOE_TRY(after_launch(launch_router(desc->dtype == MOE_BF16 ? 0 : 1, x, weights->w_router, prev_logits, logits, part,
+                                     p.nsplit, desc->S, desc->d, p.E_r, st),
                        desc, st));
-  MOE_TRY(do_route(desc, p, logits, false, routing, ws, st));
+  MOE_TRY(do_route(desc, p, logits, false, routing, ws, st, part, prev_logits));
   float* y_perm = (float*)(w + p.o_yp);
   float* y_shared = (float*)(w + p.o_ys);
   MOE_TRY(do_experts(desc, p, x, nullptr, routing, weights, y_perm, y_shared, ws, st));

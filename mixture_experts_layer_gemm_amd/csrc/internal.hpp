@@ -27,9 +27,14 @@ bool take(const char* name, hipEvent_t* start, hipEvent_t* stop);
   } while (0)
 
 // ---------------------------------------------------------------------------------------------
-// Router: logits[S, E] = x[S, d] . W_r[E, d]^T (+ prev[S, E]).
+// Router: logits[S, E] = x[S, d] . W_r[E, d]^T (+ prev[S, E]). With nsplit = router_splits(...) > 1
+// the router writes nsplit partial sums over K to part[nsplit][S][E] instead; logits are then
+// (their sum in split order) + prev, formed by launch_router_sum or by the one-workgroup routing.
+int router_splits(int dtype, int S, int d, int E);
 hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits,
-                         int S, int d, int E, hipStream_t st);
+                         float* part, int nsplit, int S, int d, int E, hipStream_t st);
+hipError_t launch_router_sum(const float* part, int nsplit, const float* prev, float* logits, int n,
+                             hipStream_t st);
 
 // ---------------------------------------------------------------------------------------------
 // Routing.
@@ -46,6 +51,12 @@ struct RouteArgs {
   uint8_t* reuse;          // [S] (nullable when tau == 0)
   float* votes;            // DES [E_r]: summed filtered probabilities (DES-Vote) or selection counts (DES-Seq)
   int32_t* core;           // DES-Vote [m_core]; DES-Seq [E_r], the union ascending then -1
+  // one-workgroup routing only: with part set, keys = (sum of nsplit router partial sums, in split
+  // order) + prev, written to logits
+  const float* part;       // [nsplit][S][E_r] (nullable)
+  int nsplit;
+  const float* prev;       // [S][E_r] (nullable)
+  float* logits;           // [S][E_r]
 };
 hipError_t launch_route_topk(const RouteArgs& a, hipStream_t st);
 hipError_t launch_route_des(const RouteArgs& a, float* ws_filt /* [S,E_r] */, hipStream_t st);

@@ -33,10 +33,12 @@ namespace moe {
 // operand Q = x rows (16 tokens): each lane ends with 4 consecutive experts of one token. x is read
 // once from HBM per expert slice; W_r stays in cache, and each of its fragments serves the TT
 // token tiles (with many experts its cache reads would otherwise outnumber those of x).
+// With nsplit > 1 (grid.z = nsplit) workgroup z takes the z-th of nsplit equal K ranges and writes
+// its sums to out + z * S * E, without prev; the splits are added later in split order.
 template <typename T, int ET, int TT>
 __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const T* __restrict__ w,
                                                  const float* __restrict__ prev, float* __restrict__ logits,
-                                                 int S, int d, int E) {
+                                                 int S, int d, int E, int nsplit) {
   constexpr int EPC = Elem<T>::kPer16B;
   constexpr int STEP = 4 * EPC;   // K elements per MFMA step
   constexpr int EW = ET * 16;     // experts per workgroup
@@ -47,9 +49,11 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
   const int r = lane & 15, g = lane >> 4;
   const int s0 = blockIdx.x * TW;
   const int e0 = blockIdx.y * EW;
+  const int nsteps = d / STEP / nsplit;                    // K steps of this workgroup
+  const size_t kz = (size_t)blockIdx.z * nsteps * STEP;   // start of its K range
   const T* xrow[TT];
 #pragma unroll
-  for (int p = 0; p < TT; ++p) xrow[p] = x + (size_t)min(s0 + p * 16 + r, S - 1) * d + g * EPC;
+  for (int p = 0; p < TT; ++p) xrow[p] = x + (size_t)min(s0 + p * 16 + r, S - 1) * d + kz + g * EPC;
   const T* wrow[ET];
   bool wok[ET];
   floatx4_t acc[TT][ET];
@@ -57,24 +61,50 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
   for (int q = 0; q < ET; ++q) {
     const int e = e0 + q * 16 + r;
     wok[q] = e < E;
-    wrow[q] = w + (size_t)min(e, E - 1) * d + g * EPC;
+    wrow[q] = w + (size_t)min(e, E - 1) * d + kz + g * EPC;
 #pragma unroll
     for (int p = 0; p < TT; ++p) acc[p][q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const int nsteps = d / STEP;
-  // a wave takes about four K steps: unrolled, all of their loads are in flight together
-#pragma unroll 4
-  for (int t = wave; t < nsteps; t += W) {
-    const size_t kk = (size_t)t * STEP;
-    uint4 xv[TT];
+  // a wave takes about four K steps. The one-tile workgroup loads U = 4 of them before it multiplies
+  // any, so their loads are in flight together (steps past the end load the last one again and are
+  // not multiplied); the wider tiles, which serve many tokens, keep the registers for occupancy.
+  // The accumulation order is step order either way.
+  constexpr int U = ET * TT == 1 ? 4 : 1;
+  if constexpr (U == 1) {
+    // one step at a time, each weight fragment used as it arrives
+    for (int t = wave; t < nsteps; t += W) {
+      const size_t kk = (size_t)t * STEP;
+      uint4 xv[TT];
 #pragma unroll
-    for (int p = 0; p < TT; ++p) xv[p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
+      for (int p = 0; p < TT; ++p) xv[p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
 #pragma unroll
-    for (int q = 0; q < ET; ++q) {
-      uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
-      if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < ET; ++q) {
+        uint4 wv = *reinterpret_cast<const uint4*>(wrow[q] + kk);
+        if (!wok[q]) wv = make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(wv, xv[p], acc[p][q], T());
+        for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(wv, xv[p], acc[p][q], T());
+      }
+    }
+  } else
+  for (int t0 = wave; t0 < nsteps; t0 += U * W) {
+    uint4 xv[U][TT], wv[U][ET];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t kk = (size_t)min(t0 + u * W, nsteps - 1) * STEP;
+#pragma unroll
+      for (int p = 0; p < TT; ++p) xv[u][p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
+#pragma unroll
+      for (int q = 0; q < ET; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wrow[q] + kk);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (t0 + u * W >= nsteps) break;   // uniform over the wave
+#pragma unroll
+      for (int q = 0; q < ET; ++q) {
+        const uint4 w = wok[q] ? wv[u][q] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(w, xv[u][p], acc[p][q], T());
+      }
     }
   }
   float* mine = s_part + (size_t)wave * TW * EW;
@@ -86,49 +116,84 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
       for (int t = 0; t < 4; ++t) mine[(p * 16 + r) * EW + q * 16 + 4 * g + t] = acc[p][q][t];
   __syncthreads();
   const int ne = min(EW, E - e0);
+  float* out = logits + (size_t)blockIdx.z * S * E;
   for (int o = threadIdx.x; o < TW * ne; o += blockDim.x) {
     const int tr = o / ne, el = o - tr * ne;
     const int st = s0 + tr, e = e0 + el;
     if (st >= S) continue;
     float v = 0.f;
     for (int q = 0; q < W; ++q) v += s_part[((size_t)q * TW + tr) * EW + el];
-    if (prev) v += prev[(size_t)st * E + e];
-    logits[(size_t)st * E + e] = v;
+    if (prev && nsplit == 1) v += prev[(size_t)st * E + e];
+    out[(size_t)st * E + e] = v;
   }
 }
 
+// logits = (sum over the K splits, in split order) + prev
+__global__ void k_router_sum(const float* __restrict__ part, int nsplit, const float* __restrict__ prev,
+                             float* __restrict__ logits, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = 0.f;
+  for (int z = 0; z < nsplit; ++z) v += part[(size_t)z * n + i];
+  if (prev) v += prev[i];
+  logits[i] = v;
+}
+
 template <typename T, int ET, int TT>
-static void router_t(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
-                     hipStream_t st) {
+static void router_t(const void* x, const void* w_router, const float* prev, float* out, int S, int d, int E,
+                     int nsplit, hipStream_t st) {
   constexpr int STEP = 4 * Elem<T>::kPer16B;
-  const int nsteps = d / STEP;
+  const int nsteps = d / STEP / nsplit;
   // about 4 K steps per wave; the partial sums of all waves fit in 64 KB of LDS
   const int W = std::max(1, std::min({16, nsteps / 4, 64 / (ET * TT)}));
   const size_t lds = (size_t)W * 16 * TT * ET * 16 * sizeof(float);
-  const dim3 grid((S + 16 * TT - 1) / (16 * TT), (E + ET * 16 - 1) / (ET * 16));
+  const dim3 grid((S + 16 * TT - 1) / (16 * TT), (E + ET * 16 - 1) / (ET * 16), nsplit);
   auto kfn = k_router<T, ET, TT>;
-  MOE_LAUNCH("router", kfn, grid, 64 * W, lds, st, (const T*)x, (const T*)w_router, prev, logits, S, d, E);
+  MOE_LAUNCH("router", kfn, grid, 64 * W, lds, st, (const T*)x, (const T*)w_router, prev, out, S, d, E, nsplit);
 }
 
 template <typename T>
-static void router_dt(const void* x, const void* w_router, const float* prev, float* logits, int S, int d, int E,
-                      hipStream_t st) {
+static void router_dt(const void* x, const void* w_router, const float* prev, float* out, int S, int d, int E,
+                      int nsplit, hipStream_t st) {
   // few tokens: one 16-expert tile per workgroup, for more workgroups; many tokens: all experts in
   // one workgroup, so x is read once, and 32 tokens per workgroup, so each W_r fragment read from
   // the cache serves two token tiles
-  if (E <= 16 || S <= 1024) router_t<T, 1, 1>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 32) router_t<T, 2, 2>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 64) router_t<T, 4, 2>(x, w_router, prev, logits, S, d, E, st);
-  else if (E <= 128) router_t<T, 8, 2>(x, w_router, prev, logits, S, d, E, st);
-  else router_t<T, 16, 1>(x, w_router, prev, logits, S, d, E, st);   // two tiles would spill
+  if (E <= 16 || S <= 1024) router_t<T, 1, 1>(x, w_router, prev, out, S, d, E, nsplit, st);
+  else if (E <= 32) router_t<T, 2, 2>(x, w_router, prev, out, S, d, E, 1, st);
+  else if (E <= 64) router_t<T, 4, 2>(x, w_router, prev, out, S, d, E, 1, st);
+  else if (E <= 128) router_t<T, 8, 2>(x, w_router, prev, out, S, d, E, 1, st);
+  else router_t<T, 16, 1>(x, w_router, prev, out, S, d, E, 1, st);   // two tiles would spill
 }
 
-hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits, int S,
-                         int d, int E, hipStream_t st) {
+// A workgroup of the one-tile router reads 16 rows of x and 16 of W_r over all of K (128 KB at
+// d = 2048 in bf16), and its waves wait on that one compute unit's loads: with few tiles (a decode
+// block: 2 x 4) most of the chip idles. Then K is split over 2 or 4 workgroups per tile (at most
+// 128 workgroups, at least 8 K steps each).
+int router_splits(int dtype, int S, int d, int E) {
+  if (S <= 0 || !(E <= 16 || S <= 1024)) return 1;
+  const int nsteps = d / (dtype == 0 ? 32 : 16);
+  const int tiles = ((S + 15) / 16) * ((E + 15) / 16);
+  int ks = 1;
+  while (ks < 4 && tiles * ks * 2 <= 128 && nsteps % (ks * 2) == 0 && nsteps / (ks * 2) >= 8) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router(int dtype, const void* x, const void* w_router, const float* prev, float* logits,
+                         float* part, int nsplit, int S, int d, int E, hipStream_t st) {
   if (S <= 0) return hipSuccess;
   if (E < 1 || E > 256) return hipErrorInvalidValue;
-  if (dtype == 0) router_dt<bf16_t>(x, w_router, prev, logits, S, d, E, st);
-  else router_dt<float>(x, w_router, prev, logits, S, d, E, st);
+  if (nsplit != 1 && (nsplit != router_splits(dtype, S, d, E) || !part)) return hipErrorInvalidValue;
+  float* out = nsplit > 1 ? part : logits;
+  if (dtype == 0) router_dt<bf16_t>(x, w_router, prev, out, S, d, E, nsplit, st);
+  else router_dt<float>(x, w_router, prev, out, S, d, E, nsplit, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_sum(const float* part, int nsplit, const float* prev, float* logits, int n,
+                             hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  auto kfn = k_router_sum;
+  MOE_LAUNCH("router_sum", kfn, (n + 255) / 256, 256, 0, st, part, nsplit, prev, logits, n);
   return hipGetLastError();
 }
 
@@ -162,19 +227,25 @@ __device__ __forceinline__ void group_argbest(float& key, int& idx) {
 
 constexpr int kMaxV = 4;   // E_r <= 256
 
-// Per-token probabilities from logits (softmax with the row max subtracted) or as given.
+// Per-token probabilities from logits (softmax with the row max subtracted) or as given. Returns
+// the token's largest probability, max(0, p): after the max subtraction the largest key's term is
+// exp(0) = 1, so that is 1 / (sum of the terms), with no further reduction.
 template <int LPT, int V>
-__device__ __forceinline__ void token_probs(const float* keys_row, bool live, int E, int sub, int input_probs,
-                                            float (&key)[V], float (&p)[V]) {
+__device__ __forceinline__ float token_probs(const float* keys_row, bool live, int E, int sub, int input_probs,
+                                             float (&key)[V], float (&p)[V]) {
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int e = sub + v * LPT;
     key[v] = (live && e < E) ? keys_row[e] : -FLT_MAX;
   }
   if (input_probs) {
+    float pm = 0.f;
 #pragma unroll
-    for (int v = 0; v < V; ++v) p[v] = (sub + v * LPT < E) ? key[v] : 0.f;
-    return;
+    for (int v = 0; v < V; ++v) {
+      p[v] = (sub + v * LPT < E) ? key[v] : 0.f;
+      pm = fmaxf(pm, p[v]);
+    }
+    return group_max<LPT>(pm);
   }
   float m = -FLT_MAX;
 #pragma unroll
@@ -190,6 +261,7 @@ __device__ __forceinline__ void token_probs(const float* keys_row, bool live, in
   const float inv = 1.0f / zs;
 #pragma unroll
   for (int v = 0; v < V; ++v) p[v] = z[v] * inv;
+  return inv;
 }
 
 constexpr int kMaxK = 16;
@@ -234,16 +306,12 @@ __global__ __launch_bounds__(256) void k_route_topk(RouteArgs a) {
   const bool live = s < a.S;
   const int E = a.E_r;
   float key[V], p[V];
-  token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
+  const float pm = token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
   if (live && a.probs) {
 #pragma unroll
     for (int v = 0; v < V; ++v)
       if (sub + v * LPT < E) a.probs[(size_t)s * E + sub + v * LPT] = p[v];
   }
-  float pm = 0.f;
-#pragma unroll
-  for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
-  pm = group_max<LPT>(pm);
   int sel_e[kMaxK];
   float sel_p[kMaxK];
   token_topk<LPT, V>(key, p, ~0u, E, sub, lane, a.k, sel_e, sel_p);
@@ -309,12 +377,9 @@ __global__ __launch_bounds__(256) void k_route_des(RouteArgs a, float* __restric
     const int s = base + threadIdx.x / LPT;
     const bool live = s < a.S;
     float key[V], p[V];
-    token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
+    const float pm =
+        token_probs<LPT, V>(a.keys + (size_t)min(s, a.S - 1) * E, live, E, sub, a.input_probs, key, p);
     const unsigned taken = token_topk<LPT, V>(key, p, ~0u, E, sub, lane, a.vote_k, nullptr, nullptr);
-    float pm = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
-    pm = group_max<LPT>(pm);
     if (live) {
 #pragma unroll
       for (int v = 0; v < V; ++v) {
@@ -559,6 +624,7 @@ constexpr int kSmallWaves = kSmallThreads / 64;
 constexpr int kSmallMaxSE = 8192;     // S * E_r: keys and probabilities kept in LDS
 constexpr int kSmallMaxPairs = 4096;  // S * k
 constexpr int kSmallMaxS = 2048;
+constexpr int kSmallMaxSplits = 4;    // router K splits the kernel adds itself
 static_assert(kSmallMaxPairs % kSmallThreads == 0, "whole rounds of pairs");
 
 bool route_small_supported(int S, int E_r, int k) {
@@ -570,10 +636,11 @@ bool route_small_supported(int S, int E_r, int k) {
 // which a full __syncthreads would also wait for (their results are not read back here).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Integer with the order of the float (finite values).
+// Integer with the order of the float (finite values); -0 and +0 are equal, as under a float
+// comparison.
 __device__ __forceinline__ int float_order(float f) {
   const int b = __float_as_int(f);
-  return b >= 0 ? b : b ^ 0x7fffffff;
+  return b >= 0 ? b : (b ^ 0x7fffffff) + 1;
 }
 
 // Top-k of one token whose experts span the whole wave (expert e in lane e % 64, slot e / 64),
@@ -587,13 +654,15 @@ __device__ __forceinline__ int float_order(float f) {
 template <int V>
 __device__ __forceinline__ unsigned wave_topk(const float (&key)[V], const float (&p)[V], unsigned allow, int E,
                                               int lane, int k, int* out_e, float* out_p) {
-  uint32_t u[V];   // keys as unsigned integers of the same order
+  // keys as unsigned integers of the same order; every key maps to 1 or more, so the ineligible
+  // entries take 0 and drop out of every count below (each candidate threshold is 1 or more)
+  uint32_t u[V];
   bool el[V];
   int n = 0;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    u[v] = (uint32_t)float_order(key[v]) ^ 0x80000000u;
     el[v] = lane + v * 64 < E && ((allow >> v) & 1u);
+    u[v] = el[v] ? (uint32_t)float_order(key[v]) ^ 0x80000000u : 0u;
     n += __popcll(__ballot(el[v]));
   }
   const int kq = min(k, n);
@@ -603,8 +672,9 @@ __device__ __forceinline__ unsigned wave_topk(const float (&key)[V], const float
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = T | (1u << b);
     int c = 0;
+    // the comparison's lane mask straight from the compare instruction (35: unsigned >=)
 #pragma unroll
-    for (int v = 0; v < V; ++v) c += __popcll(__ballot(el[v] && u[v] >= cand));
+    for (int v = 0; v < V; ++v) c += __popcll(__builtin_amdgcn_uicmp(u[v], cand, 35));
     if (c >= kq) T = cand;
     if (c == kq) {
       exact = true;
@@ -658,17 +728,20 @@ __device__ __forceinline__ unsigned wave_topk(const float (&key)[V], const float
 
 template <int LPT, int V, bool DES>
 __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, PermuteArgs q) {
+  // s_key holds the keys until the selections are made; the dispatch then keeps its per-(round,
+  // wave) expert counts there
   __shared__ float s_key[kSmallMaxSE];
   __shared__ float s_p[kSmallMaxSE];
   __shared__ float s_aux[DES ? kSmallMaxSE : 1];   // DES: filtered probabilities (DES-Seq: 1 per selection)
   __shared__ float s_votes[256];
-  __shared__ int s_rank[256], s_core[256];
+  __shared__ int s_core[256];
   __shared__ int s_ncore;
+  __shared__ int s_counts[256];
   __shared__ int s_idx[kSmallMaxPairs];
   __shared__ float s_w[kSmallMaxPairs];
+  __shared__ float s_wfin[kSmallMaxPairs];   // final weights (s_w is still read while they are formed)
   __shared__ uint8_t s_reuse[kSmallMaxS];
-  __shared__ int s_wcnt[kSmallWaves][256];
-  __shared__ int s_cnt[256], s_off[257], s_run[256];
+  __shared__ int s_off[257];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, E = a.E_r, SE = S * E;
   // slot stride of the routing arrays: k (token choice, DES-Seq) or min(k, m_core) (DES-Vote); the
@@ -678,13 +751,53 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
   int M = a.m_core;
   int kk = DES ? min(a.k, max(M, 1)) : a.k;
 
-  for (int i = tid; i < SE; i += kSmallThreads) s_key[i] = a.keys[i];
-  for (int e = tid; e < 256; e += kSmallThreads) {
-    s_cnt[e] = 0;
-    s_run[e] = 0;
-    s_rank[e] = 0;
+  {
+    // every load in flight at once (the index is clamped rather than the load skipped, so that the
+    // compiler does not wait for each one)
+    constexpr int LR = kSmallMaxSE / kSmallThreads;
+    float kv[LR];
+    if (a.part) {
+      // the router's K splits (at most kSmallMaxSplits) added in split order, then prev; the round
+      // and split conditions are uniform over the workgroup
+      const int ns = a.nsplit;
+      float t[LR][kSmallMaxSplits], pv[LR];
+#pragma unroll
+      for (int r = 0; r < LR; ++r) {
+        const int i = min(r * kSmallThreads + tid, SE - 1);
+        if (r * kSmallThreads < SE) {
+#pragma unroll
+          for (int z = 0; z < kSmallMaxSplits; ++z)
+            if (z < ns) t[r][z] = a.part[(size_t)z * SE + i];
+          if (a.prev) pv[r] = a.prev[i];
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < LR; ++r) {
+        float v = 0.f;
+        if (r * kSmallThreads < SE) {
+#pragma unroll
+          for (int z = 0; z < kSmallMaxSplits; ++z)
+            if (z < ns) v += t[r][z];
+          if (a.prev) v += pv[r];
+        }
+        kv[r] = v;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < LR; ++r) kv[r] = a.keys[min(r * kSmallThreads + tid, SE - 1)];
+    }
+#pragma unroll
+    for (int r = 0; r < LR; ++r)
+      if (r * kSmallThreads + tid < SE) s_key[r * kSmallThreads + tid] = kv[r];
+    // every path waits here for all the loads, so that the compiler does not take the unused ones as
+    // still in flight later on (its wait for them would also wait for the stores issued by then)
+    wait_vmem<0>();
+    if (a.part) {
+#pragma unroll
+      for (int r = 0; r < LR; ++r)
+        if (r * kSmallThreads + tid < SE) a.logits[r * kSmallThreads + tid] = kv[r];
+    }
   }
-  for (int i = tid; i < kSmallWaves * 256; i += kSmallThreads) (&s_wcnt[0][0])[i] = 0;
   lds_barrier();
 
   // probabilities: LPT lanes per token (max-subtracted softmax, or the given probabilities); then,
@@ -696,11 +809,7 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     const int s = base + tid / LPT;
     const bool live = s < S;
     float key[V], p[V];
-    token_probs<LPT, V>(s_key + min(s, S - 1) * E, live, E, sub, a.input_probs, key, p);
-    float pm = 0.f;
-#pragma unroll
-    for (int v = 0; v < V; ++v) pm = fmaxf(pm, p[v]);
-    pm = group_max<LPT>(pm);
+    const float pm = token_probs<LPT, V>(s_key + min(s, S - 1) * E, live, E, sub, a.input_probs, key, p);
     int sel_e[kMaxK];
     float sel_p[kMaxK];
     const int kq = DES ? a.vote_k : kk;   // DES: the filter; token choice: the selection
@@ -730,57 +839,43 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     }
   }
   lds_barrier();
-  if (a.probs)
-    for (int i = tid; i < SE; i += kSmallThreads) a.probs[i] = s_p[i];
-  if (a.reuse)
-    for (int s = tid; s < S; s += kSmallThreads) a.reuse[s] = s_reuse[s];
 
   if constexpr (DES) {
-    // votes, summed over tokens in ascending order
-    for (int e = tid; e < E; e += kSmallThreads) {
-      float v = 0.f;
-#pragma unroll 8
-      for (int n = 0; n < S; ++n) v += s_aux[n * E + e];
-      s_votes[e] = v;
-      a.votes[e] = v;
-    }
-    lds_barrier();
-    // core: DES-Vote: the M experts of largest vote (ties to the lower index). Expert e's rank is
-    // the number of experts before it in that order; the E x E comparisons are split over all
-    // threads (each expert gets kSmallThreads / E of them, adding partial counts into s_rank, zero
-    // from the start). DES-Seq: the experts some token selected (vote > 0). The core is then
-    // listed ascending by a prefix count over the membership flags.
-    if (!a.seq) {
-      const int per = max(1, kSmallThreads / E);   // threads per expert
-      const int span = (E + per - 1) / per;        // rivals per thread
-      for (int t = tid; t < E * per; t += kSmallThreads) {
-        const int e = t / per, part = t - e * per;
-        const float ve = s_votes[e];
-        const int o0 = part * span, o1 = min(E, o0 + span);
-        int r = 0;
-        for (int o = o0; o < o1; ++o) {
-          const float vo = s_votes[o];
-          r += (vo > ve || (vo == ve && o < e)) ? 1 : 0;
-        }
-        if (r) atomicAdd(&s_rank[e], r);
-      }
-    }
-    lds_barrier();
+    // votes and core, in one wave (expert e in lane e % 64, slot e / 64): the votes are summed over
+    // tokens in ascending order; DES-Vote: the core is the M experts first under (vote desc, e asc),
+    // found by the radix select of the token selections; DES-Seq: the experts some token selected
+    // (vote > 0). The core is then listed ascending by a prefix count over the membership bits.
     if (wave == 0) {
-      int cbase = 0;
-      for (int e0 = 0; e0 < E; e0 += 64) {
-        const int e = e0 + lane;
-        const bool in = e < E && (a.seq ? s_votes[e] > 0.f : s_rank[e] < M);
-        const uint64_t m = __ballot(in);
-        if (in) {
-          const int pos = cbase + __popcll(m & lanemask_lt());
-          s_core[pos] = e;
-          a.core[pos] = e;
+      constexpr int VW = LPT == 64 ? V : 1;   // LPT < 64 only for E_r <= 32
+      float vv[VW];
+#pragma unroll
+      for (int c = 0; c < VW; ++c) {
+        const int e = lane + 64 * c;
+        float v = 0.f;
+        if (e < E) {
+#pragma unroll 8
+          for (int n = 0; n < S; ++n) v += s_aux[n * E + e];
+          s_votes[e] = v;
         }
+        vv[c] = v;
+      }
+      unsigned in_core = 0;
+      if (!a.seq) {
+        in_core = wave_topk<VW>(vv, vv, ~0u, E, lane, M, nullptr, nullptr);
+      } else {
+#pragma unroll
+        for (int c = 0; c < VW; ++c)
+          if (lane + 64 * c < E && vv[c] > 0.f) in_core |= 1u << c;
+      }
+      int cbase = 0;
+#pragma unroll
+      for (int c = 0; c < VW; ++c) {
+        const int e = lane + 64 * c;
+        const bool in = (in_core >> c) & 1u;
+        const uint64_t m = __ballot(in);
+        if (in) s_core[cbase + __popcll(m & lanemask_lt())] = e;
         cbase += __popcll(m);
       }
-      if (a.seq)
-        for (int j = cbase + lane; j < E; j += 64) a.core[j] = -1;
       if (lane == 0) s_ncore = cbase;
     }
     lds_barrier();
@@ -814,69 +909,89 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
     }
     lds_barrier();
   }
+
   // weights: p, or p over the sum of the chosen p in slot order; DES-Seq slots past min(k, |core|)
-  // hold expert -1 and weight 0. One thread per (token, slot) pair, each adding its token's chosen
-  // p itself in slot order; every pair is read before any is rewritten (a token's slots may span
-  // two rounds of the workgroup).
-  {
-    constexpr int RMAX = kSmallMaxPairs / kSmallThreads;
-    const int P = S * ks;
-    float wv[RMAX];
-    int ev[RMAX];
+  // hold expert -1 and weight 0. Pair p = s * ks + j is handled by thread p % kSmallThreads here and
+  // in the dispatch below, which therefore reads its own s_idx and s_wfin entries without a barrier.
+  constexpr int RMAX = kSmallMaxPairs / kSmallThreads;
+  const int P = S * ks;
 #pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      const int p = r * kSmallThreads + tid;
-      wv[r] = 0.f;
-      ev[r] = -1;
-      if (p < P) {
-        const int s = p / ks, j = p - s * ks;
-        if (j < kk) {
-          ev[r] = s_idx[p];
-          wv[r] = s_w[p];
-          if (a.renorm) {
-            float t = 0.f;
-            for (int jj = 0; jj < kk; ++jj) t += s_w[s * ks + jj];
-            wv[r] = wv[r] / t;
-          }
+  for (int r = 0; r < RMAX; ++r) {
+    const int p = r * kSmallThreads + tid;
+    if (p < P) {
+      const int s = p / ks, j = p - s * ks;
+      int e = -1;
+      float w = 0.f;
+      if (j < kk) {
+        e = s_idx[p];
+        w = s_w[p];
+        if (a.renorm) {
+          float t = 0.f;
+          for (int jj = 0; jj < kk; ++jj) t += s_w[s * ks + jj];
+          w = w / t;
         }
       }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int r = 0; r < RMAX; ++r) {
-      const int p = r * kSmallThreads + tid;
-      if (p < P) {
-        s_idx[p] = ev[r];
-        s_w[p] = wv[r];
-        a.topk_idx[p] = ev[r];
-        a.topk_w[p] = wv[r];
-      }
+      s_idx[p] = e;
+      s_wfin[p] = w;
     }
   }
-  lds_barrier();
 
-  // dispatch: pair p = s * ks + j goes to a row when its expert is heavy and s does not reuse
-  const int P = S * ks;
+  // dispatch: pair p goes to a row when its expert is heavy and its token does not reuse. Rows are
+  // ordered by (expert, pair). Each wave counts, per round of kSmallThreads pairs, how many of its
+  // pairs go to each expert (equal experts found with match-any ballots); one wave then turns the
+  // counts into the experts' offsets and, per expert, the first row of each (round, wave); a pair's
+  // row adds the lanes before it in its wave with the same expert.
+  const int EH = q.E_heavy;
   const bool use_reuse = q.reuse != nullptr;
-  auto live_pair = [&](int p, int& e) -> bool {
-    if (p >= P) {
-      e = -1;
-      return false;
+  int* s_cnt = reinterpret_cast<int*>(s_key);   // [round * kSmallWaves + wave][EH]
+  int nbits = 1;
+  while ((1 << nbits) <= EH) ++nbits;
+  int pe[RMAX], plow[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const int p = r * kSmallThreads + tid;
+    pe[r] = -1;
+    plow[r] = 0;
+    if (r * kSmallThreads >= P) continue;   // uniform over the workgroup
+    int e = p < P ? s_idx[p] : -1;
+    const bool ok = p < P && e >= 0 && e < EH && !(use_reuse && s_reuse[p / ks]);
+    const int key = ok ? e : EH;
+    uint64_t peers = ~0ull;
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      peers &= bit ? m : ~m;
     }
-    e = s_idx[p];
-    return e >= 0 && e < q.E_heavy && !(use_reuse && s_reuse[p / ks]);
-  };
-  for (int p = tid; p < P; p += kSmallThreads) {
-    int e;
-    if (live_pair(p, e)) atomicAdd(&s_cnt[e], 1);
+    const uint64_t lower = peers & lanemask_lt();
+    int* row = s_cnt + (r * kSmallWaves + wave) * EH;
+    for (int i = lane; i < EH; i += 64) row[i] = 0;
+    // a wave's LDS writes take effect in order: the leader's count lands after the zeros
+    if (ok && lower == 0) row[e] = __popcll(peers);
+    if (ok) {
+      pe[r] = e;
+      plow[r] = __popcll(lower);
+    }
   }
   lds_barrier();
-  // offsets: exclusive scan of the counts over experts (light experts count 0), one wave
   if (wave == 0) {
+    const int nslot = ((P + kSmallThreads - 1) / kSmallThreads) * kSmallWaves;
     int base = 0;
     for (int e0 = 0; e0 < E; e0 += 64) {
       const int e = e0 + lane;
-      const int c = (e < E && e < q.E_heavy) ? s_cnt[e] : 0;
+      int c = 0;
+      if (e < EH) {
+        // exclusive prefix over the (round, wave) slots, in place; c ends as the expert's count
+        for (int s0 = 0; s0 < nslot; s0 += kSmallWaves) {
+          int v[kSmallWaves];
+#pragma unroll
+          for (int w = 0; w < kSmallWaves; ++w) v[w] = s_cnt[(s0 + w) * EH + e];
+#pragma unroll
+          for (int w = 0; w < kSmallWaves; ++w) {
+            s_cnt[(s0 + w) * EH + e] = c;
+            c += v[w];
+          }
+        }
+      }
       int incl = c;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -885,55 +1000,54 @@ __global__ __launch_bounds__(kSmallThreads) void k_route_small(RouteArgs a, Perm
       }
       if (e < E) {
         s_off[e] = base + incl - c;
-        q.offsets[e] = base + incl - c;
-        q.counts[e] = c;
+        s_counts[e] = c;
       }
       base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) {
-      s_off[E] = base;
-      q.offsets[E] = base;
-      *q.n_rows = base;
-    }
+    if (lane == 0) s_off[E] = base;
   }
-  int nbits = 1;
-  while ((1 << nbits) <= q.E_heavy) ++nbits;
   lds_barrier();
-  for (int r0 = 0; r0 < P; r0 += kSmallThreads) {
-    const int p = r0 + tid;
-    int e;
-    const bool ok = live_pair(p, e);
-    const int key = ok ? e : q.E_heavy;
-    uint64_t peers = ~0ull;
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    const uint64_t lower = peers & lanemask_lt();
-    if (ok && lower == 0) s_wcnt[wave][e] = __popcll(peers);
-    lds_barrier();
-    if (ok) {
-      int base = s_off[e] + s_run[e];
-      for (int o = 0; o < wave; ++o) base += s_wcnt[o][e];
-      const int row = base + __popcll(lower);
+  // every global store comes last: a wait that the compiler places for a load would otherwise
+  // also wait for the stores issued before it
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const int p = r * kSmallThreads + tid;
+    if (p >= P) continue;
+    const int e = pe[r];
+    if (e >= 0) {
+      const int row = s_off[e] + s_cnt[(r * kSmallWaves + wave) * EH + e] + plow[r];
       q.row_token[row] = p / ks;
-      q.row_w[row] = s_w[p];
+      q.row_w[row] = s_wfin[p];
       q.token_rows[p] = row;
-    } else if (p < P) {
+    } else {
       q.token_rows[p] = -1;
     }
-    lds_barrier();
-    for (int i = tid; i < q.E_heavy; i += kSmallThreads) {
-      int add = 0;
-      for (int o = 0; o < kSmallWaves; ++o) {
-        add += s_wcnt[o][i];
-        s_wcnt[o][i] = 0;
-      }
-      s_run[i] += add;
-    }
-    lds_barrier();
   }
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const int p = r * kSmallThreads + tid;
+    if (p < P) {
+      a.topk_idx[p] = s_idx[p];
+      a.topk_w[p] = s_wfin[p];
+    }
+  }
+  for (int e = tid; e <= E; e += kSmallThreads) {
+    q.offsets[e] = s_off[e];
+    if (e < E) q.counts[e] = s_counts[e];
+    if (e == E) *q.n_rows = s_off[E];
+  }
+  if constexpr (DES) {
+    const int nc = s_ncore;
+    for (int e = tid; e < E; e += kSmallThreads) {
+      a.votes[e] = s_votes[e];
+      if (e < nc) a.core[e] = s_core[e];
+      else if (a.seq) a.core[e] = -1;
+    }
+  }
+  if (a.probs)
+    for (int i = tid; i < SE; i += kSmallThreads) a.probs[i] = s_p[i];
+  if (a.reuse)
+    for (int s = tid; s < S; s += kSmallThreads) a.reuse[s] = s_reuse[s];
 }
 
 template <int LPT, int V>
@@ -949,7 +1063,12 @@ static void route_small_t(const RouteArgs& a, const PermuteArgs& q, bool des, hi
 
 hipError_t launch_route_small(const RouteArgs& a, const PermuteArgs& q, bool des, hipStream_t st) {
   const int kk = des ? (a.seq ? a.k : std::min(a.k, a.m_core)) : a.k;
-  if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > 256 || q.k != kk) return hipErrorInvalidValue;
+  if (!route_small_supported(a.S, a.E_r, kk) || q.E_heavy > a.E_r || q.k != kk) return hipErrorInvalidValue;
+  if (a.part && (a.nsplit < 1 || a.nsplit > kSmallMaxSplits || !a.logits)) return hipErrorInvalidValue;
+  // the dispatch's per-(round, wave) expert counts live in the key array (at most 4096 entries
+  // within the limits above)
+  if ((int64_t)((a.S * kk + kSmallThreads - 1) / kSmallThreads) * kSmallWaves * q.E_heavy > kSmallMaxSE)
+    return hipErrorInvalidValue;
   const int E = a.E_r;   // the lane mapping of launch_route_topk
   if (E <= 8) route_small_t<8, 1>(a, q, des, st);
   else if (E <= 32) route_small_t<8, 4>(a, q, des, st);

@@ -33,6 +33,8 @@ def _logits(rng, S, E, scale=0.7, tie_rows=0.2):
     L = (rng.standard_normal((S, E)) * scale).astype(np.float32)
     ties = rng.random(S) < tie_rows
     L[ties] = rng.integers(-1, 2, size=(int(ties.sum()), E)).astype(np.float32)   # exact ties
+    # half of those zeros negative: -0 and +0 are equal keys, the lower expert first
+    L[(L == 0) & (rng.random((S, E)) < 0.5)] = np.float32(-0.0)
     return L
 
 
