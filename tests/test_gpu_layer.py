@@ -327,6 +327,45 @@ def test_des_with_full_cover_is_token_choice():
         assert torch.equal(y0, y1), name
 
 
+SPLIT_ROUTER_CASES = {
+    "des_vote_b025": WORKLOADS["des_vote_b025"],
+    "des_seq": WORKLOADS["des_seq"],
+    "vanilla_top8": WORKLOADS["vanilla_top8"],
+    # gate residual on a small batch: 4 K splits of 9 steps at d = 1152
+    "mmoe_s32": WORKLOADS["mmoe"].replace(S=32, n_layers=1),
+    "f32_s20": WORKLOADS["dit_moe_tiny_f32"].replace(S=20),
+}
+
+
+@pytest.mark.parametrize("name", list(SPLIT_ROUTER_CASES))
+def test_split_router_paths_agree(name):
+    """With few token tiles the router splits K over several workgroups per tile. The one-workgroup
+    routing adds the partial sums itself; the multi-launch path adds them with a summing kernel.
+    Both give the same logits (checked against the oracle, with the previous layer's logits added),
+    routing and output, bit for bit."""
+    spec = SPLIT_ROUTER_CASES[name]
+    say(f"split router {name}: S={spec.S} d={spec.d} E_r={spec.E_routed}")
+    inp = gen_layer_inputs(spec, seed=5)
+    x = dev_tensor(inp.x, inp.bits.get("x"), spec.dtype)
+    wt = upload_layer(inp)
+    prev32 = np.random.default_rng(6).standard_normal((spec.S, spec.E_routed)).astype(np.float32)
+    outs = {}
+    for with_prev in (False, True):
+        prev = torch.from_numpy(prev32).cuda() if with_prev else None
+        for multi in (False, True):
+            flags = moe.MOE_F_ROUTE_MULTI if multi else 0
+            y, logits, rb = run_layer(spec, x, wt, flags=flags, prev=prev)
+            outs[with_prev, multi] = (y, logits, routing_np(rb, spec))
+        L64 = orc.router_logits(inp.x, inp.w_router[0], prev32.astype(np.float64) if with_prev else None)
+        assert np.allclose(to_np(outs[with_prev, False][1]), L64, atol=2e-5 * max(1.0, np.abs(L64).max()))
+        (y0, l0, r0), (y1, l1, r1) = outs[with_prev, False], outs[with_prev, True]
+        assert torch.equal(l0, l1), "logits"
+        for key in ("topk_idx", "topk_w", "counts", "offsets", "row_token", "row_w", "token_rows", "n_rows"):
+            assert np.array_equal(r0[key], r1[key]), key
+        assert torch.equal(y0, y1), "output"
+    assert not torch.equal(outs[False, False][1], outs[True, False][1])
+
+
 FOUR_CALL_CASES = {
     # grouped GEMMs, then the combine kernel
     "dit_moe_xl": (WORKLOADS["dit_moe_xl"].replace(S=513), 0, False, False),
