@@ -65,11 +65,11 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
 #pragma unroll
     for (int p = 0; p < TT; ++p) acc[p][q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // a wave takes about four K steps. The one-tile workgroup loads U = 4 of them before it multiplies
-  // any, so their loads are in flight together (steps past the end load the last one again and are
-  // not multiplied); the wider tiles, which serve many tokens, keep the registers for occupancy.
-  // The accumulation order is step order either way.
-  constexpr int U = ET * TT == 1 ? 4 : 1;
+  // a wave takes about four K steps. It loads U of them before it multiplies any, so their loads
+  // are in flight together (steps past the end load the last one again and are not multiplied):
+  // 4 in the one-tile workgroup, 2 with 2 x 2 tiles; the widest tiles keep one step at a time, for
+  // their registers. The accumulation order is step order whatever U is.
+  constexpr int U = ET * TT == 1 ? 4 : (ET * TT <= 4 ? 2 : 1);
   if constexpr (U == 1) {
     // one step at a time, each weight fragment used as it arrives
     for (int t = wave; t < nsteps; t += W) {
