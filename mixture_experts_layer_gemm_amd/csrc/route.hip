@@ -85,25 +85,26 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
         for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(wv, xv[p], acc[p][q], T());
       }
     }
-  } else
-  for (int t0 = wave; t0 < nsteps; t0 += U * W) {
-    uint4 xv[U][TT], wv[U][ET];
+  } else {
+    for (int t0 = wave; t0 < nsteps; t0 += U * W) {
+      uint4 xv[U][TT], wv[U][ET];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t kk = (size_t)min(t0 + u * W, nsteps - 1) * STEP;
+      for (int u = 0; u < U; ++u) {
+        const size_t kk = (size_t)min(t0 + u * W, nsteps - 1) * STEP;
 #pragma unroll
-      for (int p = 0; p < TT; ++p) xv[u][p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
+        for (int p = 0; p < TT; ++p) xv[u][p] = *reinterpret_cast<const uint4*>(xrow[p] + kk);
 #pragma unroll
-      for (int q = 0; q < ET; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wrow[q] + kk);
-    }
+        for (int q = 0; q < ET; ++q) wv[u][q] = *reinterpret_cast<const uint4*>(wrow[q] + kk);
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (t0 + u * W >= nsteps) break;   // uniform over the wave
+      for (int u = 0; u < U; ++u) {
+        if (t0 + u * W >= nsteps) break;   // uniform over the wave
 #pragma unroll
-      for (int q = 0; q < ET; ++q) {
-        const uint4 w = wok[q] ? wv[u][q] : make_uint4(0, 0, 0, 0);
+        for (int q = 0; q < ET; ++q) {
+          const uint4 w = wok[q] ? wv[u][q] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(w, xv[u][p], acc[p][q], T());
+          for (int p = 0; p < TT; ++p) acc[p][q] = mfma16(w, xv[u][p], acc[p][q], T());
+        }
       }
     }
   }
