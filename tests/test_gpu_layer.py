@@ -334,6 +334,9 @@ SPLIT_ROUTER_CASES = {
     # gate residual on a small batch: 4 K splits of 9 steps at d = 1152
     "mmoe_s32": WORKLOADS["mmoe"].replace(S=32, n_layers=1),
     "f32_s20": WORKLOADS["dit_moe_tiny_f32"].replace(S=20),
+    # one token, and a block of 5: one token tile, every split
+    "vanilla_s1": WORKLOADS["vanilla_top8"].replace(S=1),
+    "des_s5": WORKLOADS["des_vote_b025"].replace(S=5),
 }
 
 
