@@ -49,6 +49,18 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
   const int r = lane & 15, g = lane >> 4;
   const int s0 = blockIdx.x * TW;
   const int e0 = blockIdx.y * EW;
+  const int ne = min(EW, E - e0);
+  // the previous layer's logits for this thread's first PF outputs, loaded before the K loop so
+  // that the epilogue does not wait a memory round trip for them (the rest are read there)
+  constexpr int PF = 2;
+  const bool add_prev = prev && nsplit == 1;
+  float pre[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int o = threadIdx.x + i * blockDim.x;
+    const int tr = o / ne, st = s0 + tr;
+    pre[i] = add_prev && o < TW * ne && st < S ? prev[(size_t)st * E + e0 + (o - tr * ne)] : 0.f;
+  }
   const int nsteps = d / STEP / nsplit;                    // K steps of this workgroup
   const size_t kz = (size_t)blockIdx.z * nsteps * STEP;   // start of its K range
   const T* xrow[TT];
@@ -116,17 +128,22 @@ __global__ __launch_bounds__(1024) void k_router(const T* __restrict__ x, const 
 #pragma unroll
       for (int t = 0; t < 4; ++t) mine[(p * 16 + r) * EW + q * 16 + 4 * g + t] = acc[p][q][t];
   __syncthreads();
-  const int ne = min(EW, E - e0);
   float* out = logits + (size_t)blockIdx.z * S * E;
-  for (int o = threadIdx.x; o < TW * ne; o += blockDim.x) {
+  auto finish = [&](int o, float pv, bool have) {
     const int tr = o / ne, el = o - tr * ne;
     const int st = s0 + tr, e = e0 + el;
-    if (st >= S) continue;
+    if (st >= S) return;
     float v = 0.f;
     for (int q = 0; q < W; ++q) v += s_part[((size_t)q * TW + tr) * EW + el];
-    if (prev && nsplit == 1) v += prev[(size_t)st * E + e];
+    if (add_prev) v += have ? pv : prev[(size_t)st * E + e];
     out[(size_t)st * E + e] = v;
+  };
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    const int o = threadIdx.x + i * blockDim.x;
+    if (o < TW * ne) finish(o, pre[i], true);
   }
+  for (int o = threadIdx.x + PF * blockDim.x; o < TW * ne; o += blockDim.x) finish(o, 0.f, false);
 }
 
 // logits = (sum over the K splits, in split order) + prev
