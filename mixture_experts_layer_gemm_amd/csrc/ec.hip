@@ -32,7 +32,19 @@ __global__ __launch_bounds__(kProbTok * kProbLanes) void k_ec_probs(ECArgs a) {
   const int s0 = blockIdx.x * kProbTok;
   const int ns = min(kProbTok, a.S - s0);
   const float* kb = a.keys + (size_t)s0 * E;
-  for (int i = threadIdx.x; i < ns * E; i += NT) s_blk[(i / E) * ld + i % E] = kb[i];
+  // eight loads in flight per thread (the index is clamped rather than the load skipped, so that the
+  // compiler does not wait for each one before its LDS store)
+  const int n = ns * E;
+  for (int i0 = threadIdx.x; i0 < n; i0 += 8 * NT) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = kb[min(i0 + j * NT, n - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j * NT;
+      if (i < n) s_blk[(i / E) * ld + i % E] = v[j];
+    }
+  }
   __syncthreads();
   const int t = threadIdx.x / kProbLanes, q = threadIdx.x % kProbLanes;
   if (!a.input_probs) {   // uniform: all lanes of a group take part in the shuffles
@@ -199,25 +211,32 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
 // the workgroup's first token is the sum of the counts before it (read directly: S ints), then a
 // workgroup scan; the first workgroup also writes the fixed per-expert counts / offsets.
 constexpr int kCsrTok = 256;
+constexpr int kCsrPre = 32;   // experts whose row entries a thread loads before anything else
 
 __global__ __launch_bounds__(kCsrTok) void k_ec_csr(ECArgs a) {
   __shared__ int s_w[2 * (kCsrTok / 64)];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int s0 = blockIdx.x * kCsrTok;
+  // this token's rows of the first kCsrPre experts go out first, with the count loads below
+  const int sc = min(s0 + (int)threadIdx.x, a.S - 1);
+  int pre[kCsrPre];
+#pragma unroll
+  for (int j = 0; j < kCsrPre; ++j) pre[j] = a.tok_rows_tmp[(size_t)min(j, a.E - 1) * a.S + sc];
+  const int s = s0 + threadIdx.x;
+  const int c_raw = a.tok_cnt[sc];
   int before = 0;
-  int i = threadIdx.x;
-  for (; i + 7 * kCsrTok < s0; i += 8 * kCsrTok) {   // eight loads in flight (s0 is a multiple of kCsrTok)
-    int v[8];
+  // 32 loads in flight per round (s0 is a multiple of kCsrTok, so the masks are uniform over the
+  // workgroup; the masked ones read a valid count and add nothing)
+  for (int i0 = 0; i0 < s0; i0 += 32 * kCsrTok) {
+    int v[32];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = a.tok_cnt[i + j * kCsrTok];
+    for (int j = 0; j < 32; ++j) v[j] = a.tok_cnt[min(i0 + j * kCsrTok, s0 - kCsrTok) + threadIdx.x];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) before += v[j];
+    for (int j = 0; j < 32; ++j) before += i0 + j * kCsrTok < s0 ? v[j] : 0;
   }
-  for (; i < s0; i += kCsrTok) before += a.tok_cnt[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
-  const int s = s0 + threadIdx.x;
-  const int c = s < a.S ? a.tok_cnt[s] : 0;
+  const int c = s < a.S ? c_raw : 0;
   int incl = c;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -233,7 +252,10 @@ __global__ __launch_bounds__(kCsrTok) void k_ec_csr(ECArgs a) {
   int pos = base + incl - c;
   if (s < a.S) {
     a.token_off[s] = pos;
-    for (int e0 = 0; e0 < a.E; e0 += 8) {   // eight loads in flight, then the writes in expert order
+#pragma unroll
+    for (int j = 0; j < kCsrPre; ++j)
+      if (j < a.E && pre[j] >= 0) a.token_list[pos++] = pre[j];
+    for (int e0 = kCsrPre; e0 < a.E; e0 += 8) {   // eight loads in flight, then the writes in expert order
       int r[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) r[j] = e0 + j < a.E ? a.tok_rows_tmp[(size_t)(e0 + j) * a.S + s] : -1;
