@@ -147,11 +147,20 @@ struct step_sched {
   }
 };
 
-// WV waves per workgroup: 4 (one per SIMD, each wave 128 x BN/2 outputs) or 8 (two per SIMD, each
-// 128 x BN/4: a wave that stalls on a load, an LDS read or the barrier leaves the matrix core to the
-// other wave of its SIMD).
+// The LDS ring: five 32 KB units, one array per unit, so that with the K loop unrolled every LDS
+// access names its unit at compile time. They are all of LDS; nothing else in the GEMM kernels uses
+// LDS, and each kernel that uses them gets its own copy.
+static_assert(kUnits == 5, "the ring below is written for five units");
+__shared__ __attribute__((aligned(16))) uint8_t smem0[kUnitB];
+__shared__ __attribute__((aligned(16))) uint8_t smem1[kUnitB];
+__shared__ __attribute__((aligned(16))) uint8_t smem2[kUnitB];
+__shared__ __attribute__((aligned(16))) uint8_t smem3[kUnitB];
+__shared__ __attribute__((aligned(16))) uint8_t smem4[kUnitB];
+
+// One 256 x BN tile of problem P: m-tile rows [row0, row0 + rows) of group g, n-tile nt.
 template <typename T, int KIND, int ACT, int BN, int WV>
-__global__ __launch_bounds__(64 * WV, 1) void k_grouped_gemm(GemmLaunch args) {
+__device__ __forceinline__ void gemm_tile(const GemmProblem& P, const int g, const int row0, const int rows,
+                                          const int nt) {
   constexpr int EPC = Elem<T>::kPer16B;        // elements per 16-byte chunk
   constexpr int BK = kStepB / sizeof(T);       // K elements per MFMA step
   constexpr int BU = 2 * BK;                   // K elements per unit (one K block)
@@ -165,38 +174,7 @@ __global__ __launch_bounds__(64 * WV, 1) void k_grouped_gemm(GemmLaunch args) {
   static_assert(BN % (16 * WN) == 0 && (!SWIGLU || NI % 2 == 0), "whole n-subtiles per wave (gate and up halves)");
   static_assert(A_LD * kRowsPerLoad * WV == kBM && B_LD * kRowsPerLoad * WV == BN, "whole loads per unit");
   static_assert(kBM * kRowB <= kUnitB && BN * kRowB <= kUnitB, "a unit holds one K block of A or of B");
-  // One array per ring unit: with the K loop unrolled every LDS access names its unit at compile
-  // time. Five 32 KB units are all of LDS; nothing else in the kernel uses LDS.
-  static_assert(kUnits == 5, "the ring below is written for five units");
-  __shared__ __attribute__((aligned(16))) uint8_t smem0[kUnitB];
-  __shared__ __attribute__((aligned(16))) uint8_t smem1[kUnitB];
-  __shared__ __attribute__((aligned(16))) uint8_t smem2[kUnitB];
-  __shared__ __attribute__((aligned(16))) uint8_t smem3[kUnitB];
-  __shared__ __attribute__((aligned(16))) uint8_t smem4[kUnitB];
 
-  // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
-  // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
-  // contiguous chunks, one per XCD, swept as kGM m-tiles x all n-tiles, which keeps an expert's
-  // weight panels and token panels in one L2. An XCD runs its chunk of problem 0 (the one with the
-  // longer K, placed there by the host) and then its chunk of problem 1; workgroups beyond both
-  // chunks (the grid is sized from upper bounds on the row counts) exit at once.
-  const int mtl0 = mtile_total(args.p0), mtl1 = args.slots1 ? mtile_total(args.p1) : 0;
-  const int live0 = mtl0 * args.tiles_n0, live1 = mtl1 * args.tiles_n1;
-  const int c0 = (live0 + 7) >> 3, c1 = (live1 + 7) >> 3;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const bool second = slot >= c0;
-  const int Lq = second ? xcd * c1 + (slot - c0) : xcd * c0 + slot;
-  if (second ? (slot - c0 >= c1 || Lq >= live1) : Lq >= live0) return;
-  const GemmProblem P = second ? args.p1 : args.p0;   // a copy: kept in scalar registers
-  const int tn = second ? args.tiles_n1 : args.tiles_n0;
-  const int mt_live = second ? mtl1 : mtl0;
-  const int grp = Lq / (kGM * tn);
-  const int rem = Lq - grp * kGM * tn;
-  const int gsz = min(kGM, mt_live - grp * kGM);
-  const int mt = grp * kGM + rem % gsz;
-  const int nt = rem / gsz;
-  int g, row0, rows;
-  if (!mtile_locate(P, mt, g, row0, rows)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -560,6 +538,46 @@ __global__ __launch_bounds__(64 * WV, 1) void k_grouped_gemm(GemmLaunch args) {
   }
 }
 
+// WV waves per workgroup: 4 (one per SIMD, each wave 128 x BN/2 outputs) or 8 (two per SIMD, each
+// 128 x BN/4: a wave that stalls on a load, an LDS read or the barrier leaves the matrix core to the
+// other wave of its SIMD).
+template <typename T, int KIND, int ACT, int BN, int WV>
+__global__ __launch_bounds__(64 * WV, 1) void k_grouped_gemm(GemmLaunch args) {
+  // ---- tile decode. Workgroups are dealt to the 8 XCDs round robin (workgroup b to XCD b % 8), in
+  // order. The tiles of each problem that exist (m-tiles counted from the offsets) are cut into 8
+  // contiguous chunks, one per XCD, swept as kGM m-tiles x all n-tiles, which keeps an expert's
+  // weight panels and token panels in one L2. An XCD runs its chunk of problem 0 (the one with the
+  // longer K, placed there by the host) and then its chunk of problem 1; workgroups beyond both
+  // chunks (the grid is sized from upper bounds on the row counts) exit at once.
+  const int mtl0 = mtile_total(args.p0), mtl1 = args.slots1 ? mtile_total(args.p1) : 0;
+  const int live0 = mtl0 * args.tiles_n0, live1 = mtl1 * args.tiles_n1;
+  const int c0 = (live0 + 7) >> 3, c1 = (live1 + 7) >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const bool second = slot >= c0;
+  const int Lq = second ? xcd * c1 + (slot - c0) : xcd * c0 + slot;
+  if (second ? (slot - c0 >= c1 || Lq >= live1) : Lq >= live0) return;
+  const GemmProblem P = second ? args.p1 : args.p0;   // a copy: kept in scalar registers
+  const int tn = second ? args.tiles_n1 : args.tiles_n0;
+  const int mt_live = second ? mtl1 : mtl0;
+  const int grp = Lq / (kGM * tn);
+  const int rem = Lq - grp * kGM * tn;
+  const int gsz = min(kGM, mt_live - grp * kGM);
+  const int mt = grp * kGM + rem % gsz;
+  const int nt = rem / gsz;
+  int g, row0, rows;
+  if (!mtile_locate(P, mt, g, row0, rows)) return;
+  // A last column tile that is at most half used (N = 1152 with 256-wide tiles: 4.5 tiles) runs the
+  // 128-wide body: the same columns at about two thirds of the time, where the 256-wide body would
+  // multiply a half tile of repeated weight rows (for the fp32 down projection).
+  if constexpr (KIND == GEMM_DOWN && BN == 256 && WV == 4 && sizeof(T) == 2) {
+    if (nt == tn - 1 && P.N - nt * BN <= BN / 2) {
+      gemm_tile<T, KIND, ACT, BN / 2, WV>(P, g, row0, rows, 2 * nt);
+      return;
+    }
+  }
+  gemm_tile<T, KIND, ACT, BN, WV>(P, g, row0, rows, nt);
+}
+
 static int out_cols_per_tile(int kind, int act, int BN) { return (kind == GEMM_UP && act == ACT_SWIGLU) ? BN / 2 : BN; }
 
 // Tile width. The time of a launch is modelled as (rounds of one tile per compute unit) x (time of
@@ -589,8 +607,16 @@ static int64_t est_mtiles(const GemmProblem& p, int64_t rows_ub, const int64_t* 
   return std::max<int64_t>(1, (rows_ub + kBM - 1) / kBM + p.G / 2);
 }
 
-static int pick_bn(int kind, int act, const GemmProblem* probs, const int64_t* rows_ub, const int64_t* mt_hint,
-                   int nprob) {
+// Column tiles of one m-tile, in units of a tile of width bn; a last 256-wide tile that is at most half
+// used runs the 128-wide body (bf16 down projection) and counts at that body's cost.
+static double col_tiles(int N, int c, int bn, bool half_tile) {
+  if (half_tile && bn == 256 && N % 256 != 0 && N % 256 <= 128)
+    return N / 256 + (double)tile_cost(128) / tile_cost(256);
+  return (N + c - 1) / c;
+}
+
+static int pick_bn(int kind, int act, bool half_tile, const GemmProblem* probs, const int64_t* rows_ub,
+                   const int64_t* mt_hint, int nprob) {
   for (int i = 0; i < nprob; ++i)
     if (probs[i].N <= 0 || probs[i].N % 64 != 0) return 0;
   int kmin = probs[0].K;
@@ -604,7 +630,7 @@ static int pick_bn(int kind, int act, const GemmProblem* probs, const int64_t* r
     double units = 0.0;   // tiles, weighted by K / kmin (a round is one tile of the shortest K)
     for (int i = 0; i < nprob; ++i)
       units += (double)est_mtiles(probs[i], rows_ub[i], mt_hint ? mt_hint + i : nullptr) *
-               ((probs[i].N + c - 1) / c) * probs[i].K / kmin;
+               col_tiles(probs[i].N, c, bn, half_tile) * probs[i].K / kmin;
     const double t = std::ceil(units / (double)cus - 1e-9) * tile_cost(bn);
     if (best == 0 || t < best_t) {
       best = bn;
@@ -660,7 +686,7 @@ hipError_t launch_grouped_gemm(int dtype, int kind, int act, const GemmProblem* 
   for (int i = 0; i < nprob; ++i)
     if (probs[i].K <= 0 || probs[i].K % bu != 0 || probs[i].k_seg <= 0 || probs[i].k_seg % bu != 0)
       return hipErrorInvalidValue;
-  const int bn = pick_bn(kind, act, probs, rows_ub, mt_hint, nprob);
+  const int bn = pick_bn(kind, act, kind == GEMM_DOWN && dtype == 0, probs, rows_ub, mt_hint, nprob);
   if (bn == 0) return hipErrorInvalidValue;
   // the problem with the longer K goes first (see the tile decode in the kernel)
   const int first = (nprob == 2 && probs[1].K > probs[0].K) ? 1 : 0;
