@@ -193,6 +193,15 @@ def test_single_expert_layer_is_a_dense_mlp(mode):
         assert rt["C"] == spec.S
 
 
+@pytest.mark.parametrize("d", [1088, 1216])
+def test_down_projection_column_remainders(d):
+    """Model widths whose last 256-wide output tile of the down projection is a quarter used (1088 =
+    4 x 256 + 64: that tile runs the 128-wide body, half of it past N) or three quarters used (1216:
+    the 256-wide body). 6000 tokens make the 256-wide tiles the planner's choice."""
+    spec = WORKLOADS["dit_moe_xl"].replace(S=6000, d=d, f=512)
+    _layer_case(spec)
+
+
 def test_light_experts_only_layer():
     """No heavy experts: identity, zero and constant experts plus a shared expert."""
     spec = WORKLOADS["mmoe"].replace(S=500, d=256, f=512, E_heavy=0, n_layers=1)
