@@ -8,7 +8,8 @@
 // Kernels: (1) per block of 64 tokens (4 lanes per token), the probabilities, staged through LDS so
 // that both the token-major output and the expert-major copy pT[E][S] are written with coalesced
 // stores; (2) one workgroup per expert: exact radix select of the C-th largest key (the fp32 bit
-// pattern orders non-negative floats; four 8-bit digits, one LDS histogram atomic per key), then a
+// pattern orders non-negative floats; 8-bit digits from the highest bit in which the expert's keys
+// differ, one LDS histogram atomic per key), then a
 // stable compaction in token order (equal keys: lowest token first) from one workgroup-wide scan;
 // every token's row for the expert (or -1) goes to rowsT[E][S] and the token's expert count is
 // incremented; (3) the per-token row lists (CSR, ascending expert) for the combine.
@@ -16,6 +17,9 @@
 
 #include "common.hpp"
 #include "internal.hpp"
+
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_and_u32(unsigned int);
+extern "C" __device__ __attribute__((const)) unsigned int __ockl_wfred_or_u32(unsigned int);
 
 namespace moe {
 
@@ -117,6 +121,7 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
   __shared__ int hist[256];
   __shared__ int s_sel, s_rem;
   __shared__ int s_w[2 * kSelWaves];
+  __shared__ uint32_t s_bits[2 * kSelWaves];
   const int e = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(a.pT + (size_t)e * a.S);
@@ -131,9 +136,46 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
     if constexpr (REG) return ureg[j];
     else return keys[s_beg + j];
   };
-  uint32_t prefix = 0, pmask = 0;
+  // Bits in which every key of the expert agrees (where the AND and the OR of the keys are equal)
+  // hold the same value in the C-th largest key. The 8-bit digits therefore start just below the
+  // highest bit in which keys differ: with probabilities of one magnitude the top byte is the same
+  // for every key, and a first histogram over it would send every LDS atomic to one bin, where
+  // they serialise. Later digits may overlap bits already fixed; keys that pass the prefix test
+  // agree there, so the bins stay exact.
+  uint32_t k_and = ~0u, k_or = 0u;
+#pragma unroll
+  for (int j = 0; j < (REG ? kSelRegs : 1); ++j) {
+    for (int jj = REG ? j : 0; jj < (REG ? j + 1 : per); ++jj) {
+      if (REG && j >= per) break;
+      if (s_beg + jj < s_end) {
+        const uint32_t u = key(jj);
+        k_and &= u;
+        k_or |= u;
+      }
+    }
+  }
+  k_and = __ockl_wfred_and_u32(k_and);
+  k_or = __ockl_wfred_or_u32(k_or);
+  const int wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    s_bits[2 * wave] = k_and;
+    s_bits[2 * wave + 1] = k_or;
+  }
+  __syncthreads();
+  k_and = ~0u;
+  k_or = 0u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    k_and &= s_bits[2 * w];
+    k_or |= s_bits[2 * w + 1];
+  }
+  const uint32_t diff = k_and ^ k_or;   // 0: every key is the same (S >= C >= 1 keys exist)
+  const int hb = diff ? 31 - __clz((int)diff) : -1;
+  // bits above the highest differing one (all of them when every key is the same)
+  const uint32_t fixed = hb < 0 ? ~0u : hb >= 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = k_and & fixed, pmask = fixed;
   int remaining = a.C;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = max(hb - 7, 0); hb >= 0; shift = max(shift - 8, 0)) {
     for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
     __syncthreads();
 #pragma unroll
@@ -177,6 +219,7 @@ __global__ __launch_bounds__(kSelThreads) void k_ec_select(ECArgs a) {
     pmask |= 255u << shift;
     remaining = s_rem;
     __syncthreads();
+    if (shift == 0) break;
   }
   const uint32_t T = prefix;      // the C-th largest key
   const int need_eq = remaining;  // keys equal to T to take, lowest tokens first

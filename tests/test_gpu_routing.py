@@ -144,6 +144,43 @@ def test_ec_route_bitexact_on_probs(case):
     assert np.array_equal(got["token_list"][: E * C], lst)
 
 
+def _structured_ec_keys(rng, S):
+    """Columns of fp32 probabilities whose bit patterns differ in few or many bits: every key equal;
+    differing in the lowest 4 bits; in the lowest 12; softmax-like; two values with many ties; and
+    keys spread over 20 binades."""
+    base = np.float32(0.125).view(np.uint32)
+    cols = [
+        np.full(S, base, np.uint32),
+        base + rng.integers(0, 16, S).astype(np.uint32),
+        base + rng.integers(0, 4096, S).astype(np.uint32),
+        np.abs(rng.standard_normal(S) * 0.02 + 0.1).astype(np.float32).view(np.uint32),
+        np.where(rng.random(S) < 0.5, np.float32(0.25), np.float32(0.5)).astype(np.float32).view(np.uint32),
+        (np.float32(2.0) ** rng.uniform(-20, 0, S)).astype(np.float32).view(np.uint32),
+    ]
+    return np.stack(cols, axis=1).view(np.float32)
+
+
+@pytest.mark.parametrize("S", [3000, 20000])
+def test_ec_route_bitexact_structured_keys(S):
+    """Expert choice on keys whose common leading bits differ from column to column, so the radix
+    select starts at different digits (every key equal: no digit at all; a single digit that
+    overlaps no fixed bit, or several); 20000 tokens take the path that reads the keys from memory
+    on every pass."""
+    E = 6
+    spec = _spec(S=S, E_heavy=E, mode="ec", capacity_factor=1.0)
+    P32 = _structured_ec_keys(np.random.default_rng(S), S)
+    say(f"ec route structured keys S={S} E={E}")
+    got, _ = _route(spec, P32, input_probs=True)
+    C = orc.ec_capacity(S, E, 1.0)
+    tokens, gates = orc.ec_select(P32.astype(np.float64), C)
+    assert np.array_equal(got["row_token"][: E * C].reshape(E, C), tokens)
+    assert np.array_equal(got["row_w"][: E * C].reshape(E, C), gates.astype(np.float32))
+    assert np.array_equal(tokens[0], np.arange(C))   # all keys equal: the lowest tokens
+    off, lst = orc.ec_token_csr(tokens, S)
+    assert np.array_equal(got["token_off"], off)
+    assert np.array_equal(got["token_list"][: E * C], lst)
+
+
 def test_ec_route_on_logits_full_size():
     S, E = 8192, 32
     spec = _spec(S=S, E_heavy=E, mode="ec", capacity_factor=2.0)
