@@ -1,0 +1,64 @@
+"""GPU parity of the layer on a seeded sweep of shapes no workload has: model and hidden widths that
+leave ragged and half-used tiles, few or many experts, every routing mode and activation, light
+and shared experts, cache reuse and the residual add, small and mid-sized token counts (the
+one-workgroup and the multi-launch routing, the streaming and the tiled expert kernels)."""
+import numpy as np
+import pytest
+
+import oracle as orc
+from synth import LayerSpec, gen_layer_inputs
+from test_gpu_layer import _layer_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _configs(n=64, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        mode = ["tc", "tc", "tc", "ec", "des", "des_seq"][rng.integers(6)]
+        dtype = "f32" if rng.random() < 0.2 else "bf16"
+        d = int(rng.choice([64, 128, 320, 576, 1088] if dtype == "bf16" else [64, 192, 320]))
+        f = int(rng.choice([64, 192, 448, 960] if dtype == "bf16" else [128, 320]))
+        act = ["gelu", "gelu_tanh", "swiglu"][rng.integers(3)]
+        E = int(rng.integers(1, 41))
+        light = mode == "tc" and rng.random() < 0.4
+        n_id, n_zero, n_const = (int(rng.integers(0, 2)), int(rng.integers(0, 2)), int(rng.integers(0, 2))) if light \
+            else (0, 0, 0)
+        E_r = E + n_id + n_zero + n_const
+        n_shared = int(rng.integers(0, 3))
+        S = int(rng.choice([int(rng.integers(1, 70)), int(rng.integers(70, 2600))]))
+        k = int(rng.integers(1, min(E_r, 8) + 1))
+        kw = dict(name=f"rand{len(out)}", S=S, d=d, f=f, E_heavy=E, n_identity=n_id, n_zero=n_zero,
+                  n_const=n_const, n_shared=n_shared, act=act, mode=mode, k=k, renorm=bool(rng.random() < 0.7),
+                  dtype=dtype)
+        if mode == "ec":
+            fc = float(rng.choice([1.0, 2.0, 4.0]))
+            if int(np.floor(np.float32(fc) * S / E_r)) < 1:
+                continue
+            kw.update(capacity_factor=fc, k=2)
+        elif mode == "des":
+            kw.update(vote_k=int(rng.integers(1, k + 1)), m_core=int(rng.integers(1, E_r + 1)))
+        elif mode == "des_seq":
+            kw.update(vote_k=int(rng.integers(1, min(3, E_r) + 1)))
+        elif rng.random() < 0.3:
+            kw.update(reuse_tau=0.3)
+        out.append((LayerSpec(**kw), bool(rng.random() < 0.5)))
+    return out
+
+
+CONFIGS = _configs()
+
+
+@pytest.mark.parametrize("spec,residual", CONFIGS, ids=[c[0].name for c in CONFIGS])
+def test_random_layer(spec, residual):
+    seed = int(spec.name[4:]) + 11
+    if spec.reuse_tau > 0:
+        # a threshold between two middle values of the tokens' top probability, so that about half
+        # of the tokens reuse the cache (with near-uniform routing a fixed 0.3 would take them all)
+        inp = gen_layer_inputs(spec, seed=seed)
+        pmax = np.sort(orc.softmax(orc.router_logits(inp.x, inp.w_router[0])).max(axis=1))
+        m = len(pmax) // 2
+        tau = 0.5 * (pmax[m] + pmax[min(m + 1, len(pmax) - 1)]) if len(pmax) > 1 else pmax[0] * 1.5
+        spec = spec.replace(reuse_tau=float(tau))
+    _layer_case(spec, seed=seed, with_cache=spec.reuse_tau > 0, residual=residual)
