@@ -398,8 +398,13 @@ def test_four_call_path_matches_layer_forward(name):
     """moe_route + moe_dispatch + moe_expert_ffn + moe_combine == moe_layer_forward (bitwise), also
     where the layer forward fuses the combine into the streaming down projection."""
     spec, flags, with_cache, residual = FOUR_CALL_CASES[name]
+    _four_call_case(name, spec, flags, with_cache, residual, seed=4)
+
+
+def _four_call_case(name, spec, flags, with_cache, residual, seed):
+    """Runs the bf16 layer both ways and checks the four-call path against moe_layer_forward."""
     say(f"four-call {name}: S={spec.S} d={spec.d} f={spec.f} flags={flags}")
-    inp = gen_layer_inputs(spec, seed=4)
+    inp = gen_layer_inputs(spec, seed=seed)
     x = dev_tensor(inp.x, inp.bits["x"], "bf16")
     wt = upload_layer(inp)
     cache0 = None

@@ -7,7 +7,7 @@ import pytest
 
 import oracle as orc
 from synth import LayerSpec, gen_layer_inputs
-from test_gpu_layer import _layer_case
+from test_gpu_layer import _four_call_case, _layer_case
 
 pytestmark = pytest.mark.gpu
 
@@ -97,3 +97,15 @@ def test_random_layer_forced_path(spec, residual, flag):
     seed = int(spec.name[4:]) + 11
     spec = _median_tau(spec, seed)
     _layer_case(spec, seed=seed, flags=flag, with_cache=spec.reuse_tau > 0, residual=residual)
+
+
+FOUR_CALL_RANDOM = [c for c in CONFIGS if c[0].dtype == "bf16"][:24]
+
+
+@pytest.mark.parametrize("spec,residual", FOUR_CALL_RANDOM, ids=[c[0].name for c in FOUR_CALL_RANDOM])
+def test_random_four_call_path(spec, residual):
+    """moe_route + moe_dispatch + moe_expert_ffn + moe_combine equal moe_layer_forward bit for bit on
+    the sweep's bf16 shapes."""
+    seed = int(spec.name[4:]) + 11
+    spec = _median_tau(spec, seed)
+    _four_call_case(spec.name, spec, 0, spec.reuse_tau > 0, residual, seed=seed)
