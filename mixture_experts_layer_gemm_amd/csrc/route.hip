@@ -506,11 +506,15 @@ hipError_t launch_route_des(const RouteArgs& a, float* ws_filt, hipStream_t st) 
 // Counting sort of the (token, slot) pairs onto heavy experts. Pair p = s*k + j. A pair is
 // dispatched when its expert is heavy and its token does not reuse its cache. Rows are grouped by
 // expert ascending; inside an expert, by p ascending (token, then slot). Three passes, no atomics
-// on the output order: per-chunk histograms, a scan, and a ranked scatter.
+// on the output order: per-chunk histograms, a scan, and a ranked scatter. When the chunk
+// histograms are small (kPermFuseMax counts) every scatter workgroup sums them itself and the
+// scan needs no launch of its own.
 constexpr int kPermThreads = 256;
 constexpr int kPermRounds = 4;
 constexpr int kPermChunk = kPermThreads * kPermRounds;
 constexpr int kPermMaxE = 1024;
+constexpr int kPermFuseMax = 4096;   // chunk counts (chunks x heavy experts) a scatter workgroup reads
+constexpr int kPermFuseLoads = kPermFuseMax / kPermThreads;
 
 int permute_num_blocks(int S, int k) { return (int)(((int64_t)S * k + kPermChunk - 1) / kPermChunk); }
 
@@ -565,10 +569,68 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scan(PermuteArgs a, int n
   }
 }
 
-__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a, int nbits) {
+// The scan folded into the scatter (nblk * E_heavy <= kPermFuseMax): this workgroup's per-expert
+// base (the counts of the chunks before it) and every expert's first row, from the chunk counts;
+// workgroup 0 also writes offsets, counts and n_rows. Integer sums: the order does not matter.
+__device__ __forceinline__ void perm_bases(const PermuteArgs& a, int nblk, int* s_base, int* s_off) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int EH = a.E_heavy, n = nblk * EH;
+  int c[kPermFuseLoads];
+#pragma unroll
+  for (int j = 0; j < kPermFuseLoads; ++j) {
+    const int t = tid + j * kPermThreads;
+    c[j] = t < n ? a.blk_cnt[t] : 0;   // every load in flight before any is used
+  }
+  for (int i = tid; i < EH; i += kPermThreads) {
+    s_base[i] = 0;
+    s_off[i] = 0;   // the expert's total first
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPermFuseLoads; ++j) {
+    const int t = tid + j * kPermThreads;
+    if (t < n && c[j]) {
+      const int bb = t / EH, e = t - bb * EH;
+      atomicAdd(&s_off[e], c[j]);
+      if (bb < (int)blockIdx.x) atomicAdd(&s_base[e], c[j]);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // exclusive prefix of the totals over experts (light experts take no rows), 64 at a time
+    int run = 0;
+    for (int e0 = 0; e0 < a.E_r; e0 += 64) {
+      const int e = e0 + lane;
+      const int tot = e < EH ? s_off[e] : 0;
+      int incl = tot;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const int off = run + incl - tot;
+      if (e < EH) s_off[e] = off;
+      if (blockIdx.x == 0 && e < a.E_r) {
+        a.offsets[e] = off;
+        a.counts[e] = tot;
+      }
+      run += __shfl(incl, 63, 64);
+    }
+    if (blockIdx.x == 0 && lane == 0) {
+      a.offsets[a.E_r] = run;
+      *a.n_rows = run;
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a, int nbits, int nblk, int fused) {
   __shared__ int wcnt[kPermThreads / 64][kPermMaxE];
   __shared__ int run[kPermMaxE];
+  __shared__ int s_base[kPermMaxE];
+  __shared__ int s_off[kPermMaxE];
   const int wave = threadIdx.x >> 6;
+  if (fused) perm_bases(a, nblk, s_base, s_off);   // uniform over the workgroup
   for (int i = threadIdx.x; i < a.E_heavy; i += kPermThreads) {
     run[i] = 0;
     for (int w = 0; w < kPermThreads / 64; ++w) wcnt[w][i] = 0;
@@ -593,7 +655,7 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(PermuteArgs a, in
     if (ok) {
       int base = run[e];
       for (int w = 0; w < wave; ++w) base += wcnt[w][e];
-      const int row = a.offsets[e] + bbase[e] + base + rank;
+      const int row = fused ? s_off[e] + s_base[e] + base + rank : a.offsets[e] + bbase[e] + base + rank;
       a.row_token[row] = (int)(p / a.k);
       a.row_w[row] = a.topk_w[p];
       a.token_rows[p] = row;
@@ -614,17 +676,20 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t st) {
   const int nblk = permute_num_blocks(a.S, a.k);
   int nbits = 1;
   while ((1 << nbits) <= a.E_heavy) ++nbits;   // classes 0..E_heavy
+  // with few chunk counts the scatter workgroups sum them themselves; S = 0 (no chunks) still takes
+  // the scan kernel, which writes the empty offsets
+  const int fused = nblk > 0 && (int64_t)nblk * a.E_heavy <= kPermFuseMax ? 1 : 0;
   if (nblk > 0) {
     auto kfn = k_perm_count;
     MOE_LAUNCH("perm_count", kfn, nblk, kPermThreads, 0, st, a);
   }
-  {
+  if (!fused) {
     auto kfn = k_perm_scan;
     MOE_LAUNCH("perm_scan", kfn, 1, kPermThreads, 0, st, a, nblk);
   }
   if (nblk > 0) {
     auto kfn = k_perm_scatter;
-    MOE_LAUNCH("perm_scatter", kfn, nblk, kPermThreads, 0, st, a, nbits);
+    MOE_LAUNCH("perm_scatter", kfn, nblk, kPermThreads, 0, st, a, nbits, nblk, fused);
   }
   return hipGetLastError();
 }
