@@ -72,8 +72,8 @@ constexpr int kOffChunk = 16;
 __device__ __forceinline__ int tiles_of(int rows) { return (int)(((unsigned)rows + (kBM - 1)) / kBM); }
 
 // offsets[g0 .. g0 + kOffChunk] into v, for g0 < G. A whole chunk in bounds is read at immediate
-// offsets from one base (the loads merge into wide ones); in the last, partial chunk entries past G
-// are not read and are set to offsets[G], so that their groups have no rows.
+// offsets from one base (one instruction per entry, no address arithmetic); in the last, partial
+// chunk entries past G are not read and are set to offsets[G], so that their groups have no rows.
 __device__ __forceinline__ void load_chunk(scalar_i32_ptr o, int g0, int G, int (&v)[kOffChunk + 1]) {
   const scalar_i32_ptr b = o + g0;
   const int n = G - g0;
