@@ -52,6 +52,28 @@ def test_noalloc_matches_workspace_entry_point(first, second):
         say(f"  bit-identical: y {tuple(y0.shape)}, rows {int(r0['n_rows'][0])}")
 
 
+def _sweep_cases():
+    """The random-shape sweep's configurations without a cache (the entry point's calls here pass
+    none) whose workspace fits the static scratch."""
+    from test_gpu_random_layers import CONFIGS
+    return [spec for spec, _ in CONFIGS
+            if spec.reuse_tau == 0 and moe.moe_workspace_bytes(moe.desc_from_spec(spec)) <= moe.MOE_NOALLOC_SCRATCH_BYTES]
+
+
+SWEEP = _sweep_cases()
+
+
+@pytest.mark.parametrize("spec", SWEEP, ids=[s.name for s in SWEEP])
+def test_noalloc_matches_workspace_entry_point_on_the_sweep(spec):
+    """Every routing mode, precision and expert mix of the random-shape sweep: the output, the logits
+    and every routing array are bit-identical to the workspace entry point's."""
+    (y0, l0, r0), (y1, l1, r1) = _pair(spec, seed=int(spec.name[4:]) + 11)
+    assert torch.equal(l0, l1)
+    assert torch.equal(y0, y1)
+    for key, t in r0.tensors.items():
+        assert torch.equal(t, r1[key]), key
+
+
 def test_noalloc_under_graph_capture():
     """The callers it is for: a decode-block layer captured into a HIP graph through the entry point
     that allocates nothing, replayed four times with eager calls of the same entry point (other
